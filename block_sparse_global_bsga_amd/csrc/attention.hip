@@ -1,0 +1,455 @@
+// Attention kernels: block-sparse attention over the kept patch blocks
+// (equation "SparseAttn" of "Block-Sparse Global Attention for Efficient
+// Multi-View Geometry Transformers", key design 1, with masked entries
+// excluded from the softmax), the dense special-token part with its
+// log-sum-exp merge (key design 3 and the framework flowchart), and the dense
+// path (equation "Attention") used for comparison.
+//
+// One tile core serves every mode.  A workgroup of KT/32 waves owns KT query
+// rows (32 per wave) and walks a list of KT-key tiles: the kept blocks of its
+// CSR row (sparse), every tile (dense), a range of tiles (split-K for the
+// special queries) or the special-token tiles (patch queries x special keys).
+//
+// Data flow per key tile, per wave (v_mfma_f32_32x32x16_bf16 throughout):
+//   S^T (keys x queries) = K Q^T : K rows from LDS are the A operand, the
+//     wave's 32 query rows stay in registers as the B operand.  Lane l then
+//     holds the 16 scores of query l%32 for one half of each 32-key sub-tile.
+//   online softmax in float32 (exp2 with log2(e)/8 folded into one FMA).
+//   O^T (dims x queries) += V^T P^T : P^T is exactly the accumulator layout
+//     converted to bf16 (the B operand), V^T comes from LDS (A operand).
+// For P^T to be usable as the B operand without any data movement, the eight
+// keys a lane contributes to one PV instruction must be contiguous in V^T.
+// The accumulator rows of lane half hh are i = 8a + 4hh + c; loading K row
+// pi(i) (bits 2 and 3 of i swapped) into A row i makes them the keys
+// 16m + 8hh + e, e = 0..7, i.e. contiguous.
+//
+// K and V are first packed (once per layer) into "packed order": patch
+// tokens, padding, special tokens, padding (each segment a multiple of 128),
+// K as rows [H][ntot_pad][64] and V transposed as [H][64][ntot_pad], so that
+// every tile load is a contiguous, aligned, zero-padded 16-byte stream.
+#include "bsga_internal.hpp"
+
+namespace bsga {
+
+enum Mode { kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3 };
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kp;
+  const uint16_t* vt;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  uint16_t* o;
+  float* lse;
+  float* part_o;   // [H][ns_pad][nsplit][64]
+  float* part_ml;  // [H][ns_pad][nsplit][2]
+  Dims d;
+  int n_items;
+  int q_tiles;
+  int nsplit;
+  int tiles_per_split;
+};
+
+constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
+
+__device__ inline int pi_row(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+// LDS swizzles (16-byte chunk index XOR a row function) so that the MFMA
+// operand reads and the tile stores touch distinct banks.
+__device__ inline int swz_k(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 1); }
+template <int KT>
+__device__ inline int swz_v(int d) {
+  if constexpr (KT == 128) return d & 15;
+  else return ((d >> 1) & 7) ^ ((d & 1) << 2);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int KT, int MODE>
+__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs a) {
+  constexpr int NT = 2 * KT;       // threads (KT/32 waves)
+  constexpr int KCH = KT * 8;      // 16-byte chunks of a K tile
+  constexpr int VROW = KT / 8;     // chunks per V^T row
+  constexpr int VCH = 64 * VROW;   // chunks of a V^T tile
+  constexpr int PER = KCH / NT;    // chunks per thread (4)
+  constexpr int NS = KT / 32;      // 32-key sub-tiles
+  __shared__ u32x4 lk[2][KCH];
+  __shared__ u32x4 lv[2][VCH];
+
+  const Dims& d = a.d;
+  const int item = xcd_item(blockIdx.x, a.n_items);
+  if (item < 0) return;
+  const int T = threadIdx.x, w = T >> 6, lane = T & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  int h, qp0, nt, tile0 = 0, split = 0;
+  const int32_t* cols = nullptr;
+  if constexpr (MODE == kSparse) {
+    h = item / d.B;
+    qp0 = (item - h * d.B) * KT;
+    const int r0 = a.row_ptr[item];
+    cols = a.col_idx + r0;
+    nt = min(a.row_ptr[item + 1] - r0, d.B);  // a valid row never exceeds B
+  } else if constexpr (MODE == kDense) {
+    h = item / a.q_tiles;
+    qp0 = (item - h * a.q_tiles) * KT;
+    nt = d.ntot_pad / KT;
+  } else if constexpr (MODE == kSpecialSplit) {
+    const int per_h = a.q_tiles * a.nsplit;
+    h = item / per_h;
+    const int rem = item - h * per_h;
+    const int qt = rem / a.nsplit;
+    split = rem - qt * a.nsplit;
+    qp0 = d.np_pad + qt * KT;
+    tile0 = split * a.tiles_per_split;
+    nt = max(0, min(a.tiles_per_split, d.ntot_pad / KT - tile0));
+  } else {
+    h = item / a.q_tiles;
+    qp0 = (item - h * a.q_tiles) * KT;
+    tile0 = d.np_pad / KT;
+    nt = d.ns_pad / KT;
+  }
+  auto tile_kp0 = [&](int n) -> int {
+    if constexpr (MODE == kSparse) return min(max(cols[n], 0), d.B - 1) * KT;
+    else return (tile0 + n) * KT;
+  };
+  auto tile_valid = [&](int kp0) -> int {
+    return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
+  };
+
+  // the wave's 32 query rows: lane half hh holds dims [32hh, 32hh + 32)
+  const int qp = qp0 + 32 * w + l32;
+  const int qtok = packed_token(qp, d);
+  bf16x8 qop[4];
+  {
+    const u32x4* src = (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u32x4 t = u32x4{0, 0, 0, 0};
+      if (qtok >= 0) t = src[m];
+      qop[m] = as_bf16x8(t);
+    }
+  }
+
+  const u32x4* kbase = (const u32x4*)a.kp + (size_t)h * d.ntot_pad * 8;
+  const size_t vstride = (size_t)d.ntot_pad / 8;
+  const u32x4* vbase = (const u32x4*)a.vt + (size_t)h * 64 * vstride;
+  u32x4 rk[PER], rv[PER];
+  auto gload = [&](int kp0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = T + NT * i;
+      rk[i] = kbase[(size_t)(kp0 + (c >> 3)) * 8 + (c & 7)];
+      rv[i] = vbase[(size_t)(c / VROW) * vstride + kp0 / 8 + (c % VROW)];
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = T + NT * i;
+      const int row = c >> 3, ch = c & 7;
+      lk[buf][row * 8 + (ch ^ swz_k(row))] = rk[i];
+      const int dr = c / VROW, vc = c % VROW;
+      lv[buf][dr * VROW + (vc ^ swz_v<KT>(dr))] = rv[i];
+    }
+  };
+
+  f32x16 o0 = {}, o1 = {};
+  float m_run = -INFINITY, l_run = 0.f;
+  if (nt > 0) {
+    gload(tile_kp0(0));
+    sstore(0);
+  }
+  __syncthreads();
+  for (int n = 0; n < nt; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < nt) gload(tile_kp0(n + 1));
+    const int kp0 = tile_kp0(n);
+    const int valid = tile_valid(kp0);
+    if (valid > 0) {
+      f32x16 s[NS];
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        s[t] = f32x16{};
+        const int R = 32 * t + pi_row(l32);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 kop = as_bf16x8(lk[buf][R * 8 + ((4 * hh + m) ^ swz_k(R))]);
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], s[t], 0, 0, 0);
+        }
+      }
+      if (valid < KT) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+            if (key >= valid) s[t][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2((m_run - m_new) * kScaleLog2);
+      const float mb = m_new * kScaleLog2;
+      float rs = 0.f;
+      bf16x8 pp[NS][2];
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 e8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = fast_exp2(fmaf(s[t][8 * h2 + e], kScaleLog2, -mb));
+            rs += pv;
+            e8[e] = pv;
+          }
+          pp[t][h2] = __builtin_convertvector(e8, bf16x8);
+        }
+      l_run = l_run * alpha + rs;
+      o0 *= alpha;
+      o1 *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int ch = 4 * t + 2 * h2 + hh;
+          const bf16x8 v0 = as_bf16x8(lv[buf][l32 * VROW + (ch ^ swz_v<KT>(l32))]);
+          const bf16x8 v1 = as_bf16x8(lv[buf][(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pp[t][h2], o0, 0, 0, 0);
+          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pp[t][h2], o1, 0, 0, 0);
+        }
+    }
+    if (n + 1 < nt) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32]
+  const float l_tot = xor32_sum(l_run);
+  if constexpr (MODE == kSpecialSplit) {
+    const int sq = qp - d.np_pad;
+    const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
+    float4* po = (float4*)(a.part_o + slot * kHeadDim);
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      po[(8 * aa + 4 * hh) / 4] = make_float4(o0[4 * aa], o0[4 * aa + 1], o0[4 * aa + 2], o0[4 * aa + 3]);
+      po[(32 + 8 * aa + 4 * hh) / 4] = make_float4(o1[4 * aa], o1[4 * aa + 1], o1[4 * aa + 2], o1[4 * aa + 3]);
+    }
+    if (hh == 0) {
+      a.part_ml[slot * 2] = m_run;
+      a.part_ml[slot * 2 + 1] = l_tot;
+    }
+    return;
+  }
+  if (qtok < 0) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? m_run * 0.125f + logf(l_tot) : -INFINITY;
+  uint16_t* orow = a.o + ((size_t)h * d.n + qtok) * kHeadDim;
+  float* lrow = a.lse + (size_t)h * d.n + qtok;
+  float cp = 0.f, cs = inv, lse_out = lse;
+  if constexpr (MODE == kPatchSpecial) {
+    const float lse_p = *lrow;
+    const float M = fmaxf(lse_p, lse);
+    const float wp = lse_p == -INFINITY ? 0.f : expf(lse_p - M);
+    const float ws = lse == -INFINITY ? 0.f : expf(lse - M);
+    const float den = wp + ws;
+    cp = den > 0.f ? wp / den : 0.f;
+    cs = den > 0.f ? ws * inv / den : 0.f;
+    lse_out = den > 0.f ? M + logf(den) : -INFINITY;
+  }
+  auto store_half = [&](const f32x16 ou, int u) {
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      u32x2* dst = (u32x2*)(orow + 32 * u + 8 * aa + 4 * hh);
+      f32x4 x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = ou[4 * aa + c] * cs;
+      if constexpr (MODE == kPatchSpecial) {
+        const u32x2 old = *dst;
+        x[0] += cp * __uint_as_float(old[0] << 16);
+        x[1] += cp * __uint_as_float(old[0] & 0xffff0000u);
+        x[2] += cp * __uint_as_float(old[1] << 16);
+        x[3] += cp * __uint_as_float(old[1] & 0xffff0000u);
+      }
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      *dst = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+    }
+  };
+  store_half(o0, 0);
+  store_half(o1, 1);
+  if (hh == 0) *lrow = lse_out;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction for the special queries: one wave per (head, special
+// token), one lane per dimension.
+__global__ __launch_bounds__(256) void special_reduce_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             uint16_t* __restrict__ o,
+                                                             float* __restrict__ lse, Dims d,
+                                                             int nsplit) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (item >= d.H * d.ns) return;
+  const int h = item / d.ns, s = item - h * d.ns;
+  const size_t base = ((size_t)h * d.ns_pad + s) * nsplit;
+  float M = -INFINITY;
+  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, part_ml[(base + c) * 2]);
+  float L = 0.f, acc = 0.f;
+  for (int c = 0; c < nsplit; ++c) {
+    const float mc = part_ml[(base + c) * 2];
+    if (mc == -INFINITY) continue;
+    const float wgt = fast_exp2((mc - M) * kScaleLog2);
+    L += wgt * part_ml[(base + c) * 2 + 1];
+    acc += wgt * part_o[(base + c) * kHeadDim + lane];
+  }
+  const int tok = special_token(s, d);
+  o[((size_t)h * d.n + tok) * kHeadDim + lane] =
+      __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
+  if (lane == 0) lse[(size_t)h * d.n + tok] = M * 0.125f + logf(L);
+}
+
+// ---------------------------------------------------------------------------
+// Packing: K rows and transposed V in packed order, 64 keys per workgroup.
+__global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
+                                                   const uint4* __restrict__ v,
+                                                   uint4* __restrict__ kp,
+                                                   uint4* __restrict__ vt, Dims d) {
+  __shared__ uint16_t sv[64][66];
+  const int kp0 = blockIdx.x * 64, h = blockIdx.y, T = threadIdx.x;
+  const size_t src_head = (size_t)h * d.n * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int row = c >> 3, ch = c & 7;
+    const int tok = packed_token(kp0 + row, d);
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) {
+      kv = k[src_head + (size_t)tok * 8 + ch];
+      vv = v[src_head + (size_t)tok * 8 + ch];
+    }
+    kp[((size_t)h * d.ntot_pad + kp0 + row) * 8 + ch] = kv;
+    const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[row][ch * 8 + 2 * e] = (uint16_t)(wv[e] & 0xffff);
+      sv[row][ch * 8 + 2 * e + 1] = (uint16_t)(wv[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int dr = c >> 3, kc = c & 7;
+    uint32_t wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wv[e] = (uint32_t)sv[8 * kc + 2 * e][dr] | ((uint32_t)sv[8 * kc + 2 * e + 1][dr] << 16);
+    vt[(((size_t)h * 64 + dr) * d.ntot_pad + kp0) / 8 + kc] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+size_t pack_bytes(const Dims& d) {
+  return 2 * (size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t);
+}
+
+hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint16_t* kp,
+                       uint16_t* vt, hipStream_t st) {
+  pack_kernel<<<dim3(d.ntot_pad / 64, d.H), 256, 0, st>>>((const uint4*)k, (const uint4*)v,
+                                                          (uint4*)kp, (uint4*)vt, d);
+  return hipGetLastError();
+}
+
+template <int KT, int MODE>
+static hipError_t run_attn(const AttnArgs& a, hipStream_t st) {
+  attn_kernel<KT, MODE><<<xcd_grid(a.n_items), 2 * KT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+static AttnArgs base_args(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                          const uint16_t* vt, uint16_t* o, float* lse) {
+  AttnArgs a = {};
+  a.q = q;
+  a.kp = kp;
+  a.vt = vt;
+  a.o = o;
+  a.lse = lse;
+  a.d = d;
+  return a;
+}
+
+hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                              const uint16_t* vt, const int32_t* row_ptr,
+                              const int32_t* col_idx, uint16_t* o, float* lse, hipStream_t st) {
+  AttnArgs a = base_args(d, q, kp, vt, o, lse);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.n_items = d.H * d.B;
+  return d.b == 64 ? run_attn<64, kSparse>(a, st) : run_attn<128, kSparse>(a, st);
+}
+
+struct SplitPlan {
+  int q_tiles, nsplit, tps;
+};
+static SplitPlan special_plan(const Dims& d) {
+  SplitPlan p;
+  p.q_tiles = d.ns_pad / 128;
+  const int nt = d.ntot_pad / 128;
+  int want = 1024 / max(1, d.H * p.q_tiles);
+  want = max(1, min(want, nt));
+  p.tps = (nt + want - 1) / want;
+  p.nsplit = (nt + p.tps - 1) / p.tps;
+  return p;
+}
+
+size_t special_workspace(const Dims& d) {
+  if (d.ns == 0) return 0;
+  const SplitPlan p = special_plan(d);
+  const size_t slots = (size_t)d.H * d.ns_pad * p.nsplit;
+  return ((slots * kHeadDim * sizeof(float) + 255) & ~(size_t)255) + slots * 2 * sizeof(float);
+}
+
+hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                          const uint16_t* vt, uint16_t* o, float* lse, void* ws, hipStream_t st) {
+  if (d.ns == 0) return hipSuccess;
+  const SplitPlan p = special_plan(d);
+  const size_t slots = (size_t)d.H * d.ns_pad * p.nsplit;
+  AttnArgs a = base_args(d, q, kp, vt, o, lse);
+  a.part_o = (float*)ws;
+  a.part_ml = (float*)((char*)ws + ((slots * kHeadDim * sizeof(float) + 255) & ~(size_t)255));
+  a.q_tiles = p.q_tiles;
+  a.nsplit = p.nsplit;
+  a.tiles_per_split = p.tps;
+  a.n_items = d.H * p.q_tiles * p.nsplit;
+  hipError_t e = run_attn<128, kSpecialSplit>(a, st);
+  if (e != hipSuccess) return e;
+  const int items = d.H * d.ns;
+  special_reduce_kernel<<<(items + 3) / 4, 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d, p.nsplit);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnArgs b = base_args(d, q, kp, vt, o, lse);
+  b.q_tiles = d.np_pad / 128;
+  b.n_items = d.H * b.q_tiles;
+  return run_attn<128, kPatchSpecial>(b, st);
+}
+
+hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
+                        uint16_t* o, float* lse, hipStream_t st) {
+  AttnArgs a = base_args(d, q, kp, vt, o, lse);
+  a.q_tiles = d.ntot_pad / 128;
+  a.n_items = d.H * a.q_tiles;
+  return run_attn<128, kDense>(a, st);
+}
+
+}  // namespace bsga

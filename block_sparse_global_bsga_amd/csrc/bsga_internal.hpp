@@ -1,0 +1,136 @@
+// Internal declarations shared by the libbsga HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bsga.h"
+
+namespace bsga {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 64;
+constexpr int kPad = 128;  // packed segments are padded to this many keys
+
+// Exact unsigned division by a runtime constant (round-up multiplier method
+// of Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994): q = (mulhi(n, m) + n) >> l, valid for every
+// 32-bit n.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t(1) << l) < d) ++l;
+  f.l = l;
+  f.m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  return f;
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t t = __umulhi(n, f.m);
+#else
+  uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
+#endif
+  return (uint32_t)(((uint64_t)t + n) >> f.l);
+}
+
+// Layer geometry.  "Packed order" lists keys (and queries) as the N_p patch
+// tokens in patch order, zero padding up to np_pad, then the N_s special
+// tokens, padding up to np_pad + ns_pad.  Both pads are multiples of kPad.
+struct Dims {
+  int F, P, S, H, b, B;
+  int np, ns, n;
+  int np_pad, ns_pad, ntot_pad;
+  FastDiv divP, divS;
+};
+
+Dims make_dims(const bsga_shape& s);
+
+// Token row of patch p and of special token s.
+__device__ inline uint32_t patch_token(uint32_t p, const Dims& d) {
+  uint32_t f = fdiv(p, d.divP);
+  return f * (uint32_t)(d.P + d.S) + (uint32_t)d.S + (p - f * (uint32_t)d.P);
+}
+__device__ inline uint32_t special_token(uint32_t s, const Dims& d) {
+  uint32_t f = fdiv(s, d.divS);
+  return f * (uint32_t)(d.P + d.S) + (s - f * (uint32_t)d.S);
+}
+
+// Token row of packed index kp, or -1 for padding.
+__device__ inline int packed_token(int kp, const Dims& d) {
+  if (kp < d.np_pad) return kp < d.np ? (int)patch_token(kp, d) : -1;
+  int s = kp - d.np_pad;
+  return s < d.ns ? (int)special_token(s, d) : -1;
+}
+
+// XCD-aware work mapping: the hardware deals workgroup ids round-robin over
+// the 8 XCDs; give each XCD one contiguous range of work items so that
+// neighbouring items (same head, nearby query blocks) share that XCD's L2.
+// The grid must hold 8 * ceil(n / 8) workgroups; ids mapped past n return -1.
+constexpr int kXcds = 8;
+__device__ inline int xcd_item(int id, int n) {
+  int per = (n + kXcds - 1) / kXcds;
+  int item = (id % kXcds) * per + id / kXcds;
+  return item < n ? item : -1;
+}
+inline int xcd_grid(int n) { return ((n + kXcds - 1) / kXcds) * kXcds; }
+
+__device__ inline float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                            __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All pointers are device
+// pointers validated by the caller.
+hipError_t launch_pool(const Dims& d, const uint16_t* q, const uint16_t* k,
+                       float* qbar, float* kbar, hipStream_t st);
+hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar,
+                         float* probs, hipStream_t st);
+hipError_t launch_softmax(const Dims& d, float* probs, hipStream_t st);
+
+struct SelectParams {
+  int k[BSGA_MAX_HEADS];
+  double tau;
+};
+size_t select_workspace(const Dims& d);
+hipError_t launch_select(const Dims& d, const float* probs,
+                         const SelectParams& sp, int32_t* row_ptr,
+                         int32_t* col_idx, void* ws, hipStream_t st);
+
+size_t pack_bytes(const Dims& d);  // packed K and V^T
+hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v,
+                       uint16_t* kp, uint16_t* vt, hipStream_t st);
+hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q,
+                              const uint16_t* kp, const uint16_t* vt,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              uint16_t* o, float* lse, hipStream_t st);
+size_t special_workspace(const Dims& d);
+hipError_t launch_special(const Dims& d, const uint16_t* q,
+                          const uint16_t* kp, const uint16_t* vt, uint16_t* o,
+                          float* lse, void* ws, hipStream_t st);
+hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                        const uint16_t* vt, uint16_t* o, float* lse,
+                        hipStream_t st);
+
+}  // namespace bsga

@@ -1,0 +1,214 @@
+/*
+ * libbsga — block-sparse global attention for VGGT-style multi-view geometry
+ * transformers, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the page "Block-Sparse Global Attention for Efficient
+ * Multi-View Geometry Transformers" (cited below as [BSGA]): its overall
+ * framework flowchart, key design 1 (block-mask prediction; equations
+ * "Attention" and "SparseAttn"), key design 2 (Top-K + CDF two-threshold
+ * block selection) and key design 3 (special tokens take a dense path).
+ * Per-head budgets follow "HeSS: Head Sensitivity Score for Sparsity
+ * Redistribution in VGGT" (cited as [HeSS]), proposed method.
+ *
+ * Conventions for every call
+ * --------------------------
+ * Tensors (batch 1, heads outermost):
+ *   Q, K, V, O   [H][N][64] bfloat16, passed as raw bits (uint16_t), row
+ *                stride 128 bytes, 16-byte aligned device pointers.
+ *   LSE          [H][N] float32, natural log of the softmax denominator.
+ *   probs        [H][B][B] float32 row-major (block-importance distribution).
+ *   row_ptr      [H*B + 1] int32; rows are ordered head-major, then query
+ *                block; col_idx[row_ptr[r] .. row_ptr[r+1]) are the kept key
+ *                blocks of row r in ascending order.
+ * Token order: frame-major; every frame holds `special_per_frame` special
+ * tokens (camera, then registers) followed by `patches_per_frame` patch
+ * tokens in raster order.  N = frames * (patches_per_frame +
+ * special_per_frame).  Patch p (0 <= p < N_p = frames * patches_per_frame)
+ * is token (p / P) * (P + S) + S + p % P.  Patch block i holds patches
+ * [i*b, min((i+1)*b, N_p)); B = ceil(N_p / b); the last block may be partial.
+ *
+ * Ownership: the caller owns and allocates every buffer, including the
+ * workspace (size from bsga_workspace_bytes).  The library never allocates,
+ * keeps no global state and never synchronises the host; every call only
+ * enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ * returns.  Inputs are read-only.
+ *
+ * Errors: every call returns a bsga_status.  All arguments are validated on
+ * the host before anything is enqueued, so an error means nothing was
+ * launched.  BSGA_ERR_HIP reports a launch failure seen after enqueueing.
+ */
+#ifndef BSGA_H
+#define BSGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSGA_VERSION 1
+#define BSGA_MAX_HEADS 256     /* per-head budget table size */
+#define BSGA_MAX_BLOCKS 4096   /* largest B accepted by bsga_select */
+
+typedef enum bsga_status {
+  BSGA_OK = 0,
+  BSGA_ERR_INVALID_ARG = 1, /* null pointer, bad size, rho/tau out of range */
+  BSGA_ERR_UNSUPPORTED = 2, /* head_dim != 64, block not 64/128, too large */
+  BSGA_ERR_MISALIGNED = 3,  /* bf16 tensors not 16-byte aligned, others 4 */
+  BSGA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small */
+  BSGA_ERR_HIP = 5          /* a kernel launch failed */
+} bsga_status;
+
+/* Operations, for bsga_workspace_bytes. */
+typedef enum bsga_op {
+  BSGA_OP_PREDICT_MASK = 0,
+  BSGA_OP_SELECT = 1,
+  BSGA_OP_SPARSE_ATTN = 2,
+  BSGA_OP_SPECIAL_DENSE = 3,
+  BSGA_OP_DENSE_ATTN = 4,
+  BSGA_OP_LAYER = 5,
+  BSGA_OP_SPECIAL_DENSE_PACKED = 6
+} bsga_op;
+
+/* Shape of one global-attention layer.  head_dim must be 64; block (b) must
+ * be 64 or 128; frames, patches_per_frame, heads >= 1;
+ * special_per_frame >= 0. */
+typedef struct bsga_shape {
+  int32_t frames;
+  int32_t patches_per_frame;
+  int32_t special_per_frame;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t block;
+} bsga_shape;
+
+/* Library version (BSGA_VERSION). */
+int bsga_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* bsga_status_string(int status);
+
+/* B = ceil(N_p / b), the number of patch blocks ([BSGA] key design 1). */
+int bsga_num_blocks(const bsga_shape* shape, int32_t* n_blocks);
+
+/* k = floor(B (1 - rho)) ([BSGA] key design 2), evaluated exactly with rho
+ * read as a decimal on a 1e-6 grid, so that e.g. B = 2140, rho = 0.9 gives
+ * 214.  rho must lie in [0, 1]. */
+int bsga_keep_count(int32_t n_blocks, double rho, int32_t* k);
+
+/* Entries col_idx must be able to hold: H * B * B (every block kept). */
+int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries);
+
+/* Workspace bytes needed by operation `op` (a bsga_op).  The workspace must
+ * be a device buffer aligned to 256 bytes; its contents on entry do not
+ * matter and are clobbered. */
+int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes);
+
+/* Block-mask prediction ([BSGA] key design 1).
+ *   Qbar[h][i] = mean of the patch rows of block i of Q (likewise Kbar),
+ *   S = Qbar Kbar^T / sqrt(64), probs[h][i][:] = softmax of S[h][i][:].
+ * q, k: [H][N][64] bf16.  probs: [H][B][B] float32 (output).
+ * qbar, kbar: optional [H][B][64] float32 outputs (NULL to skip).
+ * Pooling accumulates in float32; the pooled-score product runs on bf16
+ * MFMA on a three-way bf16 split of the float32 means (x = x1 + x2 + x3, six
+ * cross products; error near that of a float32 product); the softmax is
+ * float32. */
+int bsga_predict_mask(const bsga_shape* shape, const uint16_t* q,
+                      const uint16_t* k, float* probs, float* qbar,
+                      float* kbar, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Two-threshold block selection ([BSGA] key design 2; [HeSS] per-head
+ * budget).  For every row (h, i) of probs: rank the B key blocks by
+ * probability descending (ties: lower block index first), let
+ * k_h = floor(B (1 - rho_h)) and n_tau the smallest n whose cumulative
+ * probability of the n top-ranked blocks is >= tau (float64 sum; tau <= 0
+ * gives 0; tau >= 1 gives B; B if never reached), and keep the first
+ * max(k_h, n_tau) ranked blocks, emitted in ascending block order.
+ *   probs: [H][B][B] float32, non-negative (device).
+ *   rho_per_head: NULL (use rho for all heads) or a HOST array of H values
+ *     in [0, 1] (requires H <= BSGA_MAX_HEADS).
+ *   rho in [0, 1]; tau any finite value.
+ *   row_ptr: [H*B+1] int32 output; col_idx: output of capacity
+ *   col_capacity >= H*B*B entries.  Requires B <= BSGA_MAX_BLOCKS. */
+int bsga_select(const bsga_shape* shape, const float* probs,
+                const double* rho_per_head, double rho, double tau,
+                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention of the patch queries over their kept patch blocks
+ * ([BSGA] equation SparseAttn, masked entries excluded from the softmax):
+ * for patch query q in block i of head h,
+ *   O[h][q] = sum_t softmax_t(Q[q].K[t] / 8) V[t],  LSE[h][q] = log sum_t e^..
+ * over the patch tokens t of the blocks col_idx[row_ptr[h*B+i] ..).  Writes
+ * only the patch rows of o and lse (special rows untouched).  An empty row
+ * gives O = 0, LSE = -inf.  bf16 MFMA, float32 online softmax. */
+int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q,
+                     const uint16_t* k, const uint16_t* v,
+                     const int32_t* row_ptr, const int32_t* col_idx,
+                     uint16_t* o, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Dense part for the special tokens ([BSGA] key design 3 and framework
+ * flowchart): special queries attend to all N tokens (their rows of o/lse
+ * are written), and patch queries attend to all special tokens; the latter
+ * result is merged in place with the patch rows already in o/lse (from
+ * bsga_sparse_attn) by log-sum-exp, giving one softmax over the union of
+ * keys.  Must follow bsga_sparse_attn on the same stream. */
+int bsga_special_dense(const bsga_shape* shape, const uint16_t* q,
+                       const uint16_t* k, const uint16_t* v, uint16_t* o,
+                       float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Dense softmax attention of every token over every token ([BSGA] equation
+ * Attention): the library's own dense path, for comparison. */
+int bsga_dense_attn(const bsga_shape* shape, const uint16_t* q,
+                    const uint16_t* k, const uint16_t* v, uint16_t* o,
+                    float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Packed K/V: the layout the attention kernels stream.  Keys are listed in
+ * "packed order" — the N_p patch tokens in patch order, zero rows up to the
+ * next multiple of 128, then the N_s special tokens, zero rows up to the next
+ * multiple of 128 (Ntot_pad keys in all) — and stored as
+ *   K rows   [H][Ntot_pad][64] bf16, followed by
+ *   V^T      [H][64][Ntot_pad] bf16 (V transposed: keys contiguous).
+ * Packing once per layer lets the sparse, special and dense calls share it.
+ * kv_packed must be a 256-byte aligned device buffer of at least
+ * bsga_packed_kv_bytes bytes. */
+int bsga_packed_kv_bytes(const bsga_shape* shape, size_t* bytes);
+int bsga_pack_kv(const bsga_shape* shape, const uint16_t* k, const uint16_t* v,
+                 void* kv_packed, size_t kv_bytes, void* stream);
+
+/* bsga_sparse_attn, bsga_special_dense and bsga_dense_attn on K/V already
+ * packed by bsga_pack_kv (same semantics; no packing inside).  The special
+ * call needs a workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)
+ * for its split-K partial results. */
+int bsga_sparse_attn_packed(const bsga_shape* shape, const uint16_t* q,
+                            const void* kv_packed, size_t kv_bytes,
+                            const int32_t* row_ptr, const int32_t* col_idx,
+                            uint16_t* o, float* lse, void* stream);
+int bsga_special_dense_packed(const bsga_shape* shape, const uint16_t* q,
+                              const void* kv_packed, size_t kv_bytes,
+                              uint16_t* o, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
+                           const void* kv_packed, size_t kv_bytes, uint16_t* o,
+                           float* lse, void* stream);
+
+/* One replaced global-attention layer ([BSGA] framework flowchart):
+ * bsga_predict_mask, bsga_select, bsga_sparse_attn and bsga_special_dense in
+ * that order on `stream`, sharing one packing of K and V.  probs, row_ptr and
+ * col_idx receive the intermediate mask (same layouts as above). */
+int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
+               const uint16_t* v, const double* rho_per_head, double rho,
+               double tau, float* probs, int32_t* row_ptr, int32_t* col_idx,
+               int64_t col_capacity, uint16_t* o, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGA_H */

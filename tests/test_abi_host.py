@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/bsga.h declares, host-only calls return the right
+values, and invalid arguments are rejected before anything is launched."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsga.h")
+
+bsga = pytest.importorskip("block_sparse_global_bsga_amd.bsga",
+                           reason="libbsga.so not built")
+lib = bsga._lib
+S = bsga.LayerShape
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(bsga_\w+)\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bsga.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert bsga.version() == 1
+    for s in range(6):
+        assert bsga.status_string(s)
+    assert bsga.status_string(99) == "unknown status"
+
+
+def test_block_and_keep_counts_match_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "keep_counts.json")))
+    for case in g["cases"]:
+        # n_patch = frames * P with one frame holding all patches
+        shape = S(frames=1, patches_per_frame=case["n_patch"], special_per_frame=5, heads=2,
+                  block=case["block"])
+        assert bsga.num_blocks(shape) == case["B"]
+        for rho, k in zip(case["rho"], case["k"]):
+            assert bsga.keep_count(case["B"], rho) == k
+
+
+def test_keep_count_matches_oracle_definition():
+    from oracle import bsga_oracle as O
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        B = int(rng.integers(0, 9000))
+        rho = float(rng.integers(0, 1_000_001)) / 1e6
+        assert bsga.keep_count(B, rho) == O.keep_count(B, rho)
+
+
+def test_capacity_and_workspace_sizes():
+    shape = S(32, 1369, 5, 16, 128)
+    assert bsga.csr_capacity(shape) == 16 * 343 * 343
+    sizes = {op: bsga.workspace_bytes(shape, op) for op in range(6)}
+    assert sizes[bsga.OP_LAYER] >= max(sizes.values()) - 1
+    assert sizes[bsga.OP_SPARSE_ATTN] >= 2 * 16 * (43904 + 256) * 64 * 2
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_shapes_rejected():
+    out = ctypes.c_int32()
+    bad = [S(0, 10, 5, 1, 64), S(1, 0, 5, 1, 64), S(1, 10, -1, 1, 64), S(1, 10, 5, 0, 64)]
+    for s in bad:
+        assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_INVALID_ARG
+    for s in [S(1, 10, 5, 1, 32), S(1, 10, 5, 1, 256)]:
+        assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
+    s = S(1, 10, 5, 1, 64, head_dim=128)
+    assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
+    assert lib.bsga_num_blocks(None, ctypes.byref(out)) == bsga.ERR_INVALID_ARG
+    # too many tokens for 32-bit packed indices
+    s = S(40000, 1369, 5, 1, 128)
+    assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
+
+
+def test_keep_count_rejects_bad_rho():
+    out = ctypes.c_int32()
+    for rho in (-0.1, 1.5, float("nan")):
+        assert lib.bsga_keep_count(10, rho, ctypes.byref(out)) == bsga.ERR_INVALID_ARG
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any launch
+
+
+def test_validation_before_launch():
+    shape = S(4, 256, 5, 4, 64)
+    sh = ctypes.byref(shape.c())
+    ws = bsga.workspace_bytes(shape, bsga.OP_LAYER)
+    cap = bsga.csr_capacity(shape)
+    # null and misaligned tensors
+    assert lib.bsga_predict_mask(sh, None, FAKE, FAKE, None, None, FAKE, ws, None) == bsga.ERR_INVALID_ARG
+    assert lib.bsga_predict_mask(sh, FAKE + 2, FAKE, FAKE, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE + 1, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    # workspace: missing, short, misaligned
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, None, ws, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, FAKE, 16, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, FAKE + 16, ws, None) == bsga.ERR_WORKSPACE
+    # select: rho / tau / capacity
+    for rho, tau in ((-0.5, 0.9), (1.01, 0.9), (float("nan"), 0.9), (0.5, float("nan"))):
+        assert lib.bsga_select(sh, FAKE, None, rho, tau, FAKE, FAKE, cap, FAKE, ws, None) \
+            == bsga.ERR_INVALID_ARG
+    assert lib.bsga_select(sh, FAKE, None, 0.5, 0.9, FAKE, FAKE, cap - 1, FAKE, ws, None) \
+        == bsga.ERR_INVALID_ARG
+    rh = (ctypes.c_double * 4)(0.5, 0.5, 2.0, 0.5)
+    assert lib.bsga_select(sh, FAKE, ctypes.cast(rh, ctypes.c_void_p), 0.5, 0.9, FAKE, FAKE, cap,
+                           FAKE, ws, None) == bsga.ERR_INVALID_ARG
+    # attention calls
+    assert lib.bsga_sparse_attn(sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, ws, None) \
+        == bsga.ERR_MISALIGNED
+    assert lib.bsga_dense_attn(sh, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == bsga.ERR_INVALID_ARG
+    assert lib.bsga_special_dense(sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_layer(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE, FAKE,
+                          FAKE, ws - 1, None) == bsga.ERR_WORKSPACE
+    # selection beyond the sort's capacity
+    big = S(1, 64 * 5000, 0, 1, 64)
+    assert lib.bsga_select(ctypes.byref(big.c()), FAKE, None, 0.5, 0.9, FAKE, FAKE, 1 << 40, FAKE,
+                           1 << 40, None) == bsga.ERR_UNSUPPORTED

@@ -1,0 +1,368 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bars (see the tolerance notes next to each check):
+* block masks (row_ptr, col_idx): bit-exact when both sides select from the
+  same float32 probabilities (the GPU's);
+* attention outputs: max |O_gpu - O_oracle| <= 2e-2 * rms(O_dense) for bf16
+  inputs, the oracle run on the GPU's mask;
+* LSE: |err| <= 2e-3 (float32 sums of exp of exactly-computed bf16 dot
+  products; the slack covers the approximate exp2 and float32 accumulation);
+* pooled means: within the float32 summation bound;
+* probabilities: |P_gpu - P_oracle| <= 1e-5 (near-float32 pooled scores).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from block_sparse_global_bsga_amd import synth
+from oracle import bsga_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 2e-3
+P_TOL = 1e-5
+
+
+def _cases():
+    c = synth.CONFIGS
+    return {
+        "tiny-4f": (lambda: synth.generate(c[1]), None),
+        "vggt-8f": (lambda: synth.generate(c[2]), 16),
+        "vggt-32f": (lambda: synth.generate(c[3]), 4),
+        "ragged-b128": (lambda: synth.random_layer(3, 10, 13, 2, 128, seed=11, kind="corr"), None),
+        "multi-frame-block-b64": (lambda: synth.random_layer(5, 5, 10, 3, 64, seed=12), None),
+        "no-special-b64": (lambda: synth.random_layer(2, 16, 16, 2, 64, seed=13, special_per_frame=0,
+                                                      kind="corr"), None),
+        "position-b128": (lambda: synth.random_layer(4, 12, 12, 2, 128, seed=14, kind="pos"), None),
+        "single-block": (lambda: synth.random_layer(1, 8, 8, 1, 128, seed=15), None),
+    }
+
+
+CASES = _cases()
+_cache = {}
+
+
+def inputs(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = CASES[name][0]()
+    return _cache[name]
+
+
+def sample_blocks(name, B, h):
+    per = CASES[name][1]
+    if per is None or per >= B:
+        return list(range(B))
+    rng = np.random.default_rng(100 + h)
+    pick = set(rng.choice(B, size=per, replace=False).tolist())
+    pick.update({0, B - 1})  # always the first and the (partial) last block
+    return sorted(pick)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_sparse_global_bsga_amd import bsga
+    return bsga
+
+
+def _upload(x):
+    from gpu_helpers import to_dev
+    return to_dev(x.q), to_dev(x.k), to_dev(x.v)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_predict_mask(lib, name):
+    from gpu_helpers import layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    say(f"[predict_mask] {name} {cfg.frames}f P={cfg.patches_per_frame} b={cfg.block}")
+    shape = layer_shape(cfg)
+    q, k, _ = _upload(x)
+    probs, qbar, kbar = lib.predict_mask(shape, q, k, want_means=True)
+    probs, qbar, kbar = (t.cpu().numpy() for t in (probs, qbar, kbar))
+    _, patch = O.token_roles(cfg.frames, cfg.patches_per_frame, cfg.special_per_frame)
+    worst_p = 0.0
+    for h in range(cfg.heads):
+        qp = synth.bf16_bits_to_f64(x.q[h][patch])
+        kp = synth.bf16_bits_to_f64(x.k[h][patch])
+        qb, kb, _, p = O.predict_head(qp, kp, cfg.block)
+        for mine, ref, rows in ((qbar[h], qb, qp), (kbar[h], kb, kp)):
+            # float32 summation bound: (n+1) u sum|x| / n per element
+            absmean = O.block_means(np.abs(rows), cfg.block)
+            n = np.array([O.block_members(rows.shape[0], cfg.block, i).shape[0]
+                          for i in range(ref.shape[0])])[:, None]
+            bound = (n + 1) * 2.0 ** -24 * absmean + 1e-30
+            assert np.all(np.abs(mine - ref) <= bound), (name, h)
+        worst_p = max(worst_p, float(np.abs(probs[h] - p).max()))
+    say(f"   max |P_gpu - P_oracle| = {worst_p:.3e}")
+    assert worst_p <= P_TOL
+
+
+SELECT_PARAMS = [("config", None), ("full", (0.0, 1.0)), ("empty", (1.0, 0.0)),
+                 ("topk-only", (0.75, 0.0)), ("cdf-only", (0.0, 0.5)),
+                 ("per-head", "per-head")]
+
+
+@pytest.mark.parametrize("name", ["tiny-4f", "vggt-8f", "vggt-32f", "ragged-b128",
+                                  "multi-frame-block-b64", "single-block"])
+@pytest.mark.parametrize("param", [p[0] for p in SELECT_PARAMS])
+def test_select_bitexact(lib, name, param):
+    import torch
+    from gpu_helpers import layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    q, k, _ = _upload(x)
+    probs = lib.predict_mask(shape, q, k)
+    rho, tau, rho_h = cfg.rho, cfg.tau, None
+    spec = dict(SELECT_PARAMS)[param]
+    if spec == "per-head":
+        rng = np.random.default_rng(5)
+        rho_h = rng.choice([0.0, 0.5, 0.75, 0.9, 0.95, 1.0], size=cfg.heads).tolist()
+    elif spec is not None:
+        rho, tau = spec
+    say(f"[select] {name} {param} rho={rho} tau={tau} rho_h={rho_h}")
+    row_ptr, col_idx = lib.select(shape, probs, rho, tau, rho_h)
+    torch.cuda.synchronize()
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy()[:rp[-1]]
+    p32 = probs.cpu().numpy()
+    ref_rp, ref_ci = O.select_blocks(p32, tau, rho, rho_h)
+    assert np.array_equal(rp, ref_rp), (name, param)
+    assert np.array_equal(ci, ref_ci), (name, param)
+
+
+def test_select_ties_and_flat_rows(lib):
+    """Uniform rows and rows with many exact ties, uploaded directly."""
+    import torch
+    from gpu_helpers import DEV, say
+    shape = lib.LayerShape(frames=1, patches_per_frame=64 * 300 - 17, special_per_frame=5,
+                           heads=3, block=64)
+    B = lib.num_blocks(shape)
+    rng = np.random.default_rng(21)
+    p = np.empty((3, B, B), dtype=np.float32)
+    p[0] = np.float32(1.0 / B)
+    lv = rng.integers(0, 4, size=(B, B)).astype(np.float64)
+    p[1] = (np.exp(lv) / np.exp(lv).sum(axis=1, keepdims=True)).astype(np.float32)
+    s = rng.standard_normal((B, B)) * 20
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    p[2] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    probs = torch.from_numpy(p).to(DEV)
+    for rho, tau in ((0.5, 0.6), (0.9, 0.99), (0.0, 0.999999), (0.97, 0.3)):
+        say(f"[select ties] rho={rho} tau={tau}")
+        row_ptr, col_idx = lib.select(shape, probs, rho, tau)
+        rp = row_ptr.cpu().numpy().astype(np.int64)
+        ref_rp, ref_ci = O.select_blocks(p, tau, rho)
+        assert np.array_equal(rp, ref_rp)
+        assert np.array_equal(col_idx.cpu().numpy()[:rp[-1]], ref_ci)
+
+
+def _rms_dense(x, blocks_per_head):
+    """rms of the oracle's dense output over the sampled rows."""
+    from gpu_helpers import oracle_rows
+    acc, cnt = 0.0, 0
+    for h, blocks in blocks_per_head.items():
+        out = oracle_rows(x, h, None, blocks)
+        o = np.stack([r[0] for r in out.values()])
+        acc += float(np.sum(o ** 2))
+        cnt += o.size
+    return (acc / cnt) ** 0.5
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_parity(lib, name):
+    """bsga_layer end to end; the oracle runs on the GPU's mask."""
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, oracle_rows, layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    say(f"[layer] {name} N={cfg.tokens} H={cfg.heads} b={cfg.block} rho={cfg.rho} tau={cfg.tau}")
+    q, k, v = _upload(x)
+    bufs = lib.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+    torch.cuda.synchronize()
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx.cpu().numpy()[:rp[-1]]
+    o = from_dev_bf16(bufs.o)
+    lse = bufs.lse.cpu().numpy()
+    B = lib.num_blocks(shape)
+    sampled = {h: sample_blocks(name, B, h) for h in range(cfg.heads)}
+    rms = _rms_dense(x, sampled)
+    worst_o = worst_l = 0.0
+    for h in range(cfg.heads):
+        kept = O.kept_lists(rp, ci, h, B)
+        out = oracle_rows(x, h, kept, sampled[h])
+        eo, el, _, _ = compare_rows(out, o[h], lse[h])
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    say(f"   max|dO| = {worst_o:.3e} = {worst_o / rms:.3e} rms(O_dense); max|dLSE| = {worst_l:.3e}")
+    assert worst_o <= O_TOL * rms
+    assert worst_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("name", ["tiny-4f", "vggt-8f", "ragged-b128", "multi-frame-block-b64",
+                                  "no-special-b64", "single-block"])
+def test_calls_match_layer(lib, name):
+    """predict -> select -> sparse_attn -> special_dense as separate calls give
+    the same bytes as bsga_layer; sparse_attn alone matches the oracle's
+    patch-only attention."""
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, oracle_rows, layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    say(f"[calls] {name}")
+    q, k, v = _upload(x)
+    bufs = lib.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+    probs = lib.predict_mask(shape, q, k)
+    row_ptr, col_idx = lib.select(shape, probs, cfg.rho, cfg.tau, x.rho_per_head)
+    o, lse = lib.sparse_attn(shape, q, k, v, row_ptr, col_idx)
+    torch.cuda.synchronize()
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy()[:rp[-1]]
+    o_np, lse_np = from_dev_bf16(o), lse.cpu().numpy()
+    B = lib.num_blocks(shape)
+    worst = 0.0
+    sampled = {h: sample_blocks(name, B, h) for h in range(cfg.heads)}
+    rms = _rms_dense(x, sampled)
+    for h in range(cfg.heads):
+        out = oracle_rows(x, h, O.kept_lists(rp, ci, h, B), sampled[h],
+                          include_special_keys=False, special_queries=False)
+        eo, el, _, _ = compare_rows(out, o_np[h], lse_np[h])
+        worst = max(worst, eo)
+        assert el <= LSE_TOL
+    say(f"   sparse-only max|dO| = {worst / rms:.3e} rms")
+    assert worst <= O_TOL * rms
+    lib.special_dense(shape, q, k, v, o, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.probs, probs)
+    assert torch.equal(bufs.row_ptr, row_ptr)
+    n = int(rp[-1])
+    assert torch.equal(bufs.col_idx[:n], col_idx[:n])
+    assert torch.equal(bufs.o.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(bufs.lse, lse)
+
+
+@pytest.mark.parametrize("name", ["tiny-4f", "vggt-8f", "vggt-32f", "ragged-b128",
+                                  "multi-frame-block-b64", "no-special-b64"])
+def test_dense_parity(lib, name):
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, oracle_rows, layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    say(f"[dense] {name}")
+    q, k, v = _upload(x)
+    o, lse = lib.dense_attn(shape, q, k, v)
+    torch.cuda.synchronize()
+    o_np, lse_np = from_dev_bf16(o), lse.cpu().numpy()
+    B = lib.num_blocks(shape)
+    sampled = {h: sample_blocks(name, B, h) for h in range(cfg.heads)}
+    worst_o = worst_l = 0.0
+    acc = cnt = 0.0
+    for h in range(cfg.heads):
+        out = oracle_rows(x, h, None, sampled[h])
+        eo, el, ms, n = compare_rows(out, o_np[h], lse_np[h])
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        acc, cnt = acc + ms * n, cnt + n
+    rms = (acc / cnt) ** 0.5
+    say(f"   max|dO| = {worst_o / rms:.3e} rms; max|dLSE| = {worst_l:.3e}")
+    assert worst_o <= O_TOL * rms and worst_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("name", ["tiny-4f", "ragged-b128", "multi-frame-block-b64"])
+def test_full_mask_is_dense(lib, name):
+    """rho = 0, tau = 1 keeps every block; the layer then equals dense
+    attention (both against the oracle's dense rows, and bit-for-bit equal
+    masks: every row lists all B blocks)."""
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, oracle_rows, layer_shape, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    say(f"[full mask] {name}")
+    q, k, v = _upload(x)
+    bufs = lib.layer(shape, q, k, v, 0.0, 1.0)
+    torch.cuda.synchronize()
+    B = lib.num_blocks(shape)
+    rp = bufs.row_ptr.cpu().numpy()
+    assert np.all(np.diff(rp) == B)
+    ci = bufs.col_idx.cpu().numpy()[:rp[-1]]
+    assert np.array_equal(ci, np.tile(np.arange(B), cfg.heads * B))
+    o, lse = from_dev_bf16(bufs.o), bufs.lse.cpu().numpy()
+    acc = cnt = worst = 0.0
+    for h in range(cfg.heads):
+        out = oracle_rows(x, h, None, list(range(B)))
+        eo, el, ms, n = compare_rows(out, o[h], lse[h])
+        worst = max(worst, eo)
+        acc, cnt = acc + ms * n, cnt + n
+        assert el <= LSE_TOL
+    assert worst <= O_TOL * (acc / cnt) ** 0.5
+
+
+def test_empty_rows_use_special_keys_only(lib):
+    """rho = 1, tau = 0 keeps no patch block: patch queries see only the
+    special tokens (a valid corner of the two thresholds)."""
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, oracle_rows, layer_shape, say
+    x = inputs("ragged-b128")
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    say("[empty rows] ragged-b128")
+    q, k, v = _upload(x)
+    bufs = lib.layer(shape, q, k, v, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert int(bufs.row_ptr[-1].item()) == 0
+    B = lib.num_blocks(shape)
+    o, lse = from_dev_bf16(bufs.o), bufs.lse.cpu().numpy()
+    for h in range(cfg.heads):
+        out = oracle_rows(x, h, [np.zeros(0, np.int64)] * B, list(range(B)))
+        eo, el, ms, _ = compare_rows(out, o[h], lse[h])
+        assert eo <= O_TOL * ms ** 0.5 and el <= LSE_TOL
+
+
+def test_layer_is_deterministic(lib):
+    import torch
+    from gpu_helpers import layer_shape, say
+    x = inputs("vggt-8f")
+    shape = layer_shape(x.cfg)
+    say("[determinism] vggt-8f")
+    q, k, v = _upload(x)
+    a = lib.layer(shape, q, k, v, x.cfg.rho, x.cfg.tau)
+    o1, l1, p1 = a.o.clone(), a.lse.clone(), a.probs.clone()
+    lib.layer(shape, q, k, v, x.cfg.rho, x.cfg.tau, bufs=a)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), a.o.view(torch.int16))
+    assert torch.equal(l1, a.lse) and torch.equal(p1, a.probs)
+
+
+def test_end_to_end_mask_vs_oracle_pipeline(lib):
+    """Reported, not gated: masks from the GPU's probabilities vs masks from
+    the oracle's own float64 probabilities; differences can only come from
+    near-ties in the ranking or the coverage threshold."""
+    import torch
+    from gpu_helpers import layer_shape, say
+    for name in ("tiny-4f", "vggt-8f", "vggt-32f"):
+        x = inputs(name)
+        cfg = x.cfg
+        shape = layer_shape(cfg)
+        q, k, _ = _upload(x)
+        probs = lib.predict_mask(shape, q, k)
+        rp, ci = lib.select(shape, probs, cfg.rho, cfg.tau)
+        torch.cuda.synchronize()
+        rp = rp.cpu().numpy().astype(np.int64)
+        ci = ci.cpu().numpy()[:rp[-1]]
+        _, patch = O.token_roles(cfg.frames, cfg.patches_per_frame, cfg.special_per_frame)
+        p64 = np.stack([O.predict_head(synth.bf16_bits_to_f64(x.q[h][patch]),
+                                       synth.bf16_bits_to_f64(x.k[h][patch]), cfg.block)[3]
+                        for h in range(cfg.heads)])
+        orp, oci = O.select_blocks(p64.astype(np.float32), cfg.tau, cfg.rho)
+        B = lib.num_blocks(shape)
+        rows = cfg.heads * B
+        diff = sum(1 for r in range(rows)
+                   if not np.array_equal(ci[rp[r]:rp[r + 1]], oci[orp[r]:orp[r + 1]]))
+        say(f"[e2e mask] {name}: {diff} of {rows} rows differ from the float64 pipeline "
+            f"(nnz gpu {rp[-1]}, oracle {orp[-1]})")
