@@ -7,9 +7,10 @@ b = 128, rho = 0.75, tau = 0.9, with the planted-correspondence generator and
 10 % sink keys (synthetic; inputs resident in HBM before timing).
 
 One step = the whole hot path through the C ABI on one stream:
-bsga_predict_mask -> bsga_select -> bsga_pack_kv -> bsga_sparse_attn_packed ->
-bsga_special_dense_packed (the kernels bsga_layer runs).  HIP events around the
-sparse-attention launch give that kernel's average duration.
+bsga_predict_mask -> bsga_select -> bsga_pack_kv -> bsga_patch_rows_packed ->
+bsga_special_rows_packed (the kernels bsga_layer runs).  HIP events around the
+patch-row launch (block-sparse attention over the kept blocks plus the special
+keys) give that kernel's average duration.
 
 Prints ONE JSON line.  `value` is the layer's effective TFLOP/s:
 4 * 64 * (computed score entries) / layer time, counting kept patch-patch
@@ -132,10 +133,10 @@ def main():
         bsga.pack_kv(shape, k, v, kv=kv)
         if ev is not None:
             ev[0].record(stream)
-        bsga.sparse_attn_packed(shape, q, kv, row_ptr, col_idx, o, lse)
+        bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
         if ev is not None:
             ev[1].record(stream)
-        bsga.special_dense_packed(shape, q, kv, o, lse, ws=ws_spec)
+        bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
 
     def timed(fn, steps, warmup, with_kernel_events=False):
         for _ in range(warmup):
@@ -163,7 +164,10 @@ def main():
     n = cfg.tokens
     density = (pp + sp) / (cfg.heads * n * n)
     layer_tflops = 4 * HEAD_DIM * (pp + sp) / (ms * 1e-3) / 1e12
-    kern_tflops = 4 * HEAD_DIM * pp / (kern_ms * 1e-3) / 1e12
+    # the patch-row kernel computes the kept patch-patch entries plus N_p x N_s
+    # special-key entries per head
+    kern_entries = pp + cfg.heads * cfg.n_patch * cfg.n_special
+    kern_tflops = 4 * HEAD_DIM * kern_entries / (kern_ms * 1e-3) / 1e12
     print(f"# layer {ms:.3f} ms, sparse kernel {kern_ms:.3f} ms ({kern_tflops:.0f} TFLOP/s), "
           f"density {density:.4f}", file=sys.stderr, flush=True)
 
@@ -191,7 +195,9 @@ def main():
                           "ms": round(ms0, 4),
                           "density": round((pp0 + sp0) / (cfg.heads * n * n), 4),
                           "speedup_vs_dense": round(dense_ms / ms0, 3),
-                          "sparse_kernel_tflops": round(4 * HEAD_DIM * pp0 / (kern0 * 1e-3) / 1e12, 1)},
+                          "sparse_kernel_tflops": round(
+                              4 * HEAD_DIM * (pp0 + cfg.heads * cfg.n_patch * cfg.n_special)
+                              / (kern0 * 1e-3) / 1e12, 1)},
         }
 
     cpu = None
@@ -219,7 +225,7 @@ def main():
                    "tau": cfg.tau, "parallelism": "none (1 GPU)"},
         "layer_frac_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "density": round(density, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128, sparse>",
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128, sparse+special keys>",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "kernel_ms": round(kern_ms, 4), "traffic": None},

@@ -36,7 +36,8 @@ EXPORTS = [
     "bsga_csr_capacity", "bsga_workspace_bytes", "bsga_predict_mask",
     "bsga_select", "bsga_sparse_attn", "bsga_special_dense", "bsga_dense_attn",
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
-    "bsga_special_dense_packed", "bsga_dense_attn_packed",
+    "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
+    "bsga_special_rows_packed",
 ]
 
 
@@ -67,6 +68,9 @@ _lib.bsga_sparse_attn_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _
 _lib.bsga_special_dense_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p,
                                            ctypes.c_size_t, _p]
 _lib.bsga_dense_attn_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p]
+_lib.bsga_patch_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p, _p, _p]
+_lib.bsga_special_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p,
+                                          ctypes.c_size_t, _p]
 _lib.bsga_layer.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p, _p,
                             ctypes.c_int64, _p, _p, _p, ctypes.c_size_t, _p]
 
@@ -305,6 +309,25 @@ def dense_attn_packed(shape: LayerShape, q, kv, o, lse):
     _check(_lib.bsga_dense_attn_packed(ctypes.byref(shape.c()), _ptr(q), _ws_ptr(kv), _ws_len(kv),
                                        _ptr(o), _ptr(lse), _stream(q.device)),
            "bsga_dense_attn_packed")
+    return o, lse
+
+
+def patch_rows_packed(shape: LayerShape, q, kv, row_ptr, col_idx, o, lse):
+    _bf16(q, "q", shape)
+    _check(_lib.bsga_patch_rows_packed(ctypes.byref(shape.c()), _ptr(q), _ws_ptr(kv), _ws_len(kv),
+                                       _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
+                                       _stream(q.device)), "bsga_patch_rows_packed")
+    return o, lse
+
+
+def special_rows_packed(shape: LayerShape, q, kv, o, lse, *, ws=None):
+    _bf16(q, "q", shape)
+    if ws is None:
+        ws = workspace(shape, OP_SPECIAL_DENSE_PACKED, q.device)
+    _check(_lib.bsga_special_rows_packed(ctypes.byref(shape.c()), _ptr(q), _ws_ptr(kv),
+                                         _ws_len(kv), _ptr(o), _ptr(lse), _ws_ptr(ws),
+                                         _ws_len(ws), _stream(q.device)),
+           "bsga_special_rows_packed")
     return o, lse
 
 

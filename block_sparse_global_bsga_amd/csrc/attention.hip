@@ -31,7 +31,14 @@
 
 namespace bsga {
 
-enum Mode { kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3 };
+// kSparse:       patch queries x kept patch blocks (patch-only result)
+// kSparseFused:  patch queries x (kept patch blocks, then every special
+//                tile) in one online softmax: the final patch rows
+// kDense:        every query x every key
+// kSpecialSplit: special queries x a range of key tiles (split-K partials)
+// kPatchSpecial: patch queries x special tiles, merged by log-sum-exp into
+//                the patch rows already in O/LSE
+enum Mode { kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4 };
 
 struct AttnArgs {
   const uint16_t* q;
@@ -87,14 +94,15 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int T = threadIdx.x, w = T >> 6, lane = T & 63;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  int h, qp0, nt, tile0 = 0, split = 0;
+  int h, qp0, nt, tile0 = 0, split = 0, nt_csr = 0;
   const int32_t* cols = nullptr;
-  if constexpr (MODE == kSparse) {
+  if constexpr (MODE == kSparse || MODE == kSparseFused) {
     h = item / d.B;
     qp0 = (item - h * d.B) * KT;
     const int r0 = a.row_ptr[item];
     cols = a.col_idx + r0;
-    nt = min(a.row_ptr[item + 1] - r0, d.B);  // a valid row never exceeds B
+    nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
+    nt = nt_csr + (MODE == kSparseFused ? d.ns_pad / KT : 0);
   } else if constexpr (MODE == kDense) {
     h = item / a.q_tiles;
     qp0 = (item - h * a.q_tiles) * KT;
@@ -115,8 +123,13 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     nt = d.ns_pad / KT;
   }
   auto tile_kp0 = [&](int n) -> int {
-    if constexpr (MODE == kSparse) return min(max(cols[n], 0), d.B - 1) * KT;
-    else return (tile0 + n) * KT;
+    if constexpr (MODE == kSparse) {
+      return min(max(cols[n], 0), d.B - 1) * KT;
+    } else if constexpr (MODE == kSparseFused) {
+      return n < nt_csr ? min(max(cols[n], 0), d.B - 1) * KT : d.np_pad + (n - nt_csr) * KT;
+    } else {
+      return (tile0 + n) * KT;
+    }
   };
   auto tile_valid = [&](int kp0) -> int {
     return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
@@ -399,6 +412,16 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   return d.b == 64 ? run_attn<64, kSparse>(a, st) : run_attn<128, kSparse>(a, st);
 }
 
+hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                             const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                             uint16_t* o, float* lse, hipStream_t st) {
+  AttnArgs a = base_args(d, q, kp, vt, o, lse);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.n_items = d.H * d.B;
+  return d.b == 64 ? run_attn<64, kSparseFused>(a, st) : run_attn<128, kSparseFused>(a, st);
+}
+
 struct SplitPlan {
   int q_tiles, nsplit, tps;
 };
@@ -420,8 +443,9 @@ size_t special_workspace(const Dims& d) {
   return ((slots * kHeadDim * sizeof(float) + 255) & ~(size_t)255) + slots * 2 * sizeof(float);
 }
 
-hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
-                          const uint16_t* vt, uint16_t* o, float* lse, void* ws, hipStream_t st) {
+hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                               const uint16_t* vt, uint16_t* o, float* lse, void* ws,
+                               hipStream_t st) {
   if (d.ns == 0) return hipSuccess;
   const SplitPlan p = special_plan(d);
   const size_t slots = (size_t)d.H * d.ns_pad * p.nsplit;
@@ -436,7 +460,13 @@ hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
   if (e != hipSuccess) return e;
   const int items = d.H * d.ns;
   special_reduce_kernel<<<(items + 3) / 4, 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d, p.nsplit);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                          const uint16_t* vt, uint16_t* o, float* lse, void* ws, hipStream_t st) {
+  if (d.ns == 0) return hipSuccess;
+  hipError_t e = launch_special_rows(d, q, kp, vt, o, lse, ws, st);
   if (e != hipSuccess) return e;
   AttnArgs b = base_args(d, q, kp, vt, o, lse);
   b.q_tiles = d.np_pad / 128;

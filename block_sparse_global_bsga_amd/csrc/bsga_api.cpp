@@ -339,6 +339,37 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q, const voi
                                  (hipStream_t)stream));
 }
 
+int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q, const void* kv,
+                           size_t kv_bytes, const int32_t* row_ptr, const int32_t* col_idx,
+                           uint16_t* o, float* lse, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_ptr(q, 16));
+  BSGA_TRY(check_packed(d, kv, kv_bytes));
+  BSGA_TRY(check_ptr(row_ptr, 4));
+  BSGA_TRY(check_ptr(col_idx, 4));
+  BSGA_TRY(check_ptr(o, 16));
+  BSGA_TRY(check_ptr(lse, 4));
+  const uint16_t* kp = (const uint16_t*)kv;
+  return hip_status(launch_patch_rows(d, q, kp, kp + (size_t)d.H * d.ntot_pad * kHeadDim,
+                                      row_ptr, col_idx, o, lse, (hipStream_t)stream));
+}
+
+int bsga_special_rows_packed(const bsga_shape* shape, const uint16_t* q, const void* kv,
+                             size_t kv_bytes, uint16_t* o, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_ptr(q, 16));
+  BSGA_TRY(check_packed(d, kv, kv_bytes));
+  BSGA_TRY(check_ptr(o, 16));
+  BSGA_TRY(check_ptr(lse, 4));
+  BSGA_TRY(check_ws(d, BSGA_OP_SPECIAL_DENSE_PACKED, ws, ws_bytes));
+  const uint16_t* kp = (const uint16_t*)kv;
+  return hip_status(launch_special_rows(d, q, kp, kp + (size_t)d.H * d.ntot_pad * kHeadDim, o,
+                                        lse, ws, (hipStream_t)stream));
+}
+
 int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                const double* rho_per_head, double rho, double tau, float* probs, int32_t* row_ptr,
                int32_t* col_idx, int64_t col_capacity, uint16_t* o, float* lse, void* ws,
@@ -366,8 +397,8 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, co
   BSGA_TRY(hip_status(launch_softmax(d, probs, st)));
   BSGA_TRY(hip_status(launch_select(d, probs, sp, row_ptr, col_idx, scratch, st)));
   BSGA_TRY(hip_status(launch_pack(d, k, v, kp, vt, st)));
-  BSGA_TRY(hip_status(launch_sparse_attn(d, q, kp, vt, row_ptr, col_idx, o, lse, st)));
-  return hip_status(launch_special(d, q, kp, vt, o, lse, scratch, st));
+  BSGA_TRY(hip_status(launch_patch_rows(d, q, kp, vt, row_ptr, col_idx, o, lse, st)));
+  return hip_status(launch_special_rows(d, q, kp, vt, o, lse, scratch, st));
 }
 
 }  // extern "C"

@@ -125,7 +125,13 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q,
                               const uint16_t* kp, const uint16_t* vt,
                               const int32_t* row_ptr, const int32_t* col_idx,
                               uint16_t* o, float* lse, hipStream_t st);
+hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                             const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                             uint16_t* o, float* lse, hipStream_t st);
 size_t special_workspace(const Dims& d);
+hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
+                               const uint16_t* vt, uint16_t* o, float* lse, void* ws,
+                               hipStream_t st);
 hipError_t launch_special(const Dims& d, const uint16_t* q,
                           const uint16_t* kp, const uint16_t* vt, uint16_t* o,
                           float* lse, void* ws, hipStream_t st);

@@ -197,9 +197,31 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
                            const void* kv_packed, size_t kv_bytes, uint16_t* o,
                            float* lse, void* stream);
 
+/* The layer's final rows in two calls on packed K/V, the way bsga_layer
+ * computes them ([BSGA] framework flowchart and key design 3, one softmax per
+ * query over its whole key set):
+ *   bsga_patch_rows_packed: every patch query attends to the patch tokens of
+ *     its kept blocks AND to every special token, in one online softmax, and
+ *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
+ *     merge in bsga_special_dense, without the intermediate bf16 rounding);
+ *   bsga_special_rows_packed: every special query attends to all N tokens
+ *     (split over key ranges, partial results combined by log-sum-exp in a
+ *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and
+ *     writes its row of o/lse.
+ * The two calls write disjoint rows and may run in either order. */
+int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q,
+                           const void* kv_packed, size_t kv_bytes,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           uint16_t* o, float* lse, void* stream);
+int bsga_special_rows_packed(const bsga_shape* shape, const uint16_t* q,
+                             const void* kv_packed, size_t kv_bytes,
+                             uint16_t* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* One replaced global-attention layer ([BSGA] framework flowchart):
- * bsga_predict_mask, bsga_select, bsga_sparse_attn and bsga_special_dense in
- * that order on `stream`, sharing one packing of K and V.  probs, row_ptr and
+ * bsga_predict_mask, bsga_select, bsga_pack_kv, bsga_patch_rows_packed and
+ * bsga_special_rows_packed in that order on `stream` (so each output row is
+ * one softmax over its key set, rounded to bf16 once).  probs, row_ptr and
  * col_idx receive the intermediate mask (same layouts as above). */
 int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
                const uint16_t* v, const double* rho_per_head, double rho,
