@@ -36,9 +36,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libbsga)")
 
 
+# Per-source extras.  The attention kernels never depend on NaN propagation
+# (masked scores are -inf, not NaN), so they run with the IEEE mode bit off,
+# which lets float max chains fold into v_max3 without canonicalising every
+# MFMA result first.
+EXTRA = {"attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -14,7 +14,7 @@
 //   S^T (keys x queries) = K Q^T : K rows from LDS are the A operand, the
 //     wave's 32 query rows stay in registers as the B operand.  Lane l then
 //     holds the 16 scores of query l%32 for one half of each 32-key sub-tile.
-//   online softmax in float32 (exp2 with log2(e)/8 folded into one FMA).
+//   softmax in float32 (exp2 with log2(e)/8 folded into one FMA).
 //   O^T (dims x queries) += V^T P^T : P^T is exactly the accumulator layout
 //     converted to bf16 (the B operand), V^T comes from LDS (A operand).
 // For P^T to be usable as the B operand without any data movement, the eight
@@ -23,10 +23,32 @@
 // pi(i) (bits 2 and 3 of i swapped) into A row i makes them the keys
 // 16m + 8hh + e, e = 0..7, i.e. contiguous.
 //
+// Instruction budget.  On gfx950 an exp2 costs about four FMAs, and every
+// score needs one exp2 and one FMA, so the softmax is kept to that minimum:
+//  * lazy running max: a tile is exponentiated against the running max
+//    directly (no rescaling of O) unless its exact max lies more than 64 log2
+//    units above it; that max comes from a v_max3 chain folded into the
+//    score computation;
+//  * the rare block (first tile, partial tile, or such a jump) masks keys
+//    past a partial block, takes the exact max and rescales O and l; full
+//    tiles never execute any masking instructions;
+//  * the first product of each score accumulator starts from the constant 0.
+// The tile loop is software-pipelined: iteration n produces the scores of
+// tile n+1 sub-tile by sub-tile next to tile n's exponentials and P V
+// products, so the MFMA pipe always has independent work beside the softmax
+// arithmetic.  K and V^T have separate two-slot LDS rings (K is fetched two
+// tiles ahead, V^T one tile ahead), one barrier per tile.
+//
 // K and V are first packed (once per layer) into "packed order": patch
 // tokens, padding, special tokens, padding (each segment a multiple of 128),
-// K as rows [H][ntot_pad][64] and V transposed as [H][64][ntot_pad], so that
-// every tile load is a contiguous, aligned, zero-padded 16-byte stream.
+// K as rows [H][ntot_pad][64] and V transposed as [H][64][ntot_pad].  Tiles
+// reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at
+// base + 16 * lane: no staging registers, no LDS store instructions); the
+// bank swizzle is applied on the global side, the lane that fills LDS chunk
+// (row, physical chunk pc) fetching logical chunk pc ^ swizzle(row).  Half
+// the waves fetch K rows, the other half V^T rows, one tile ahead.
+#include <type_traits>
+
 #include "bsga_internal.hpp"
 
 namespace bsga {
@@ -58,12 +80,23 @@ struct AttnArgs {
 };
 
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
+// A tile is exponentiated against a stale running max as long as its exact
+// max is at most 64 log2 units above it: weights up to 2^64 are exact enough
+// in float32 and bf16, and sums over any sequence length stay far below
+// float32 overflow.
+constexpr float kLazySlack = 64.f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline int pi_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 // LDS swizzles (16-byte chunk index XOR a row function) so that the MFMA
-// operand reads and the tile stores touch distinct banks.
+// operand reads touch distinct banks.
 __device__ inline int swz_k(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 1); }
 template <int KT>
 __device__ inline int swz_v(int d) {
@@ -71,27 +104,19 @@ __device__ inline int swz_v(int d) {
   else return ((d >> 1) & 7) ^ ((d & 1) << 2);
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 template <int KT, int MODE>
-__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnArgs a) {
-  constexpr int NT = 2 * KT;       // threads (KT/32 waves)
-  constexpr int KCH = KT * 8;      // 16-byte chunks of a K tile
-  constexpr int VROW = KT / 8;     // chunks per V^T row
-  constexpr int VCH = 64 * VROW;   // chunks of a V^T tile
-  constexpr int PER = KCH / NT;    // chunks per thread (4)
-  constexpr int NS = KT / 32;      // 32-key sub-tiles
-  __shared__ u32x4 lk[2][KCH];
-  __shared__ u32x4 lv[2][VCH];
+__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
+    AttnArgs a) {
+  constexpr int NS = KT / 32;       // 32-key sub-tiles
+  constexpr int VROW = KT / 8;      // 16-byte chunks per V^T row
+  constexpr int KCH = 8 * KT;       // chunks of a K tile (= chunks of a V^T tile)
+  __shared__ u32x4 smem[4 * KCH];   // K slots 0, 1 then V^T slots 0, 1
 
   const Dims& d = a.d;
   const int item = xcd_item(blockIdx.x, a.n_items);
   if (item < 0) return;
-  const int T = threadIdx.x, w = T >> 6, lane = T & 63;
+  const int T = threadIdx.x, lane = T & 63;
+  const int w = __builtin_amdgcn_readfirstlane(T >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
 
   int h, qp0, nt, tile0 = 0, split = 0, nt_csr = 0;
@@ -136,11 +161,11 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
 
   // the wave's 32 query rows: lane half hh holds dims [32hh, 32hh + 32)
-  const int qp = qp0 + 32 * w + l32;
-  const int qtok = packed_token(qp, d);
   bf16x8 qop[4];
   {
-    const u32x4* src = (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
+    const int qtok = packed_token(qp0 + 32 * w + l32, d);
+    const u32x4* src =
+        (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       u32x4 t = u32x4{0, 0, 0, 0};
@@ -149,107 +174,151 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   }
 
-  const u32x4* kbase = (const u32x4*)a.kp + (size_t)h * d.ntot_pad * 8;
-  const size_t vstride = (size_t)d.ntot_pad / 8;
-  const u32x4* vbase = (const u32x4*)a.vt + (size_t)h * 64 * vstride;
-  u32x4 rk[PER], rv[PER];
-  auto gload = [&](int kp0) {
+  // ---- direct-to-LDS tile loads into two rings (K rows, V^T rows), two
+  // slots each.  Every wave issues 4 loads of 64 x 16 B per K tile and 4 per
+  // V^T tile; load i of wave w fills chunks (4w + i) * 64 + lane of the tile.
+  // The swizzle of the row a lane fills depends on i only through i mod 2
+  // (K, and V^T of 64-key tiles) or i mod 4 (V^T of 128-key tiles), so a few
+  // per-lane byte offsets cover all loads.  Addresses are a uniform base
+  // (scalar registers) plus a 32-bit per-lane offset.
+  const char* kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * kHeadDim * 2;
+  const uint32_t vrow_bytes = (uint32_t)d.ntot_pad * 2;
+  const char* vbase = (const char*)a.vt + (size_t)h * kHeadDim * vrow_bytes;
+  uint32_t koff[2], voff[4];
+  {
+    const int r0 = lane >> 3, pc = lane & 7;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = T + NT * i;
-      rk[i] = kbase[(size_t)(kp0 + (c >> 3)) * 8 + (c & 7)];
-      rv[i] = vbase[(size_t)(c / VROW) * vstride + kp0 / 8 + (c % VROW)];
+    for (int j = 0; j < 2; ++j) koff[j] = (uint32_t)(r0 * 128 + 16 * (pc ^ swz_k(8 * j + r0)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (KT == 128) {
+        const int v0 = lane >> 4, vc = lane & 15;
+        voff[j] = (uint32_t)v0 * vrow_bytes + 16 * (vc ^ swz_v<128>(4 * j + v0));
+      } else {
+        voff[j] = (uint32_t)r0 * vrow_bytes + 16 * (pc ^ swz_v<64>(8 * (j & 1) + r0));
+      }
+    }
+  }
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  auto issue_k = [&](int kp0, int slot) {
+    lds_u32x4* dst = (lds_u32x4*)&smem[slot * KCH + w * 256];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = 4 * w + i;  // 64-chunk block of the K tile: rows 8 blk .. 8 blk + 7
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kbase + (size_t)(kp0 + 8 * blk) * 128 + koff[i & 1]),
+          (__attribute__((address_space(3))) void*)(dst + i * 64), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto issue_v = [&](int kp0, int slot) {
+    lds_u32x4* dst = (lds_u32x4*)&smem[(2 + slot) * KCH + w * 256];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = T + NT * i;
-      const int row = c >> 3, ch = c & 7;
-      lk[buf][row * 8 + (ch ^ swz_k(row))] = rk[i];
-      const int dr = c / VROW, vc = c % VROW;
-      lv[buf][dr * VROW + (vc ^ swz_v<KT>(dr))] = rv[i];
+    for (int i = 0; i < 4; ++i) {
+      const int blk = 4 * w + i;
+      const size_t row0 = KT == 128 ? 4 * blk : 8 * blk;  // first V^T row of the block
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vbase + row0 * vrow_bytes + (size_t)kp0 * 2 + voff[i & 3]),
+          (__attribute__((address_space(3))) void*)(dst + i * 64), 16, 0, 0);
     }
   };
 
+  // ---- software-pipelined tile loop.  Iteration n exponentiates tile n and
+  // accumulates its P V while the scores of tile n+1 are produced, so the
+  // MFMA pipe always has independent work next to the softmax arithmetic.
+  // Before a tile's exponentials, a uniform flag (partial tile, first tile,
+  // or its exact max more than 64 log2 units above the running max) selects
+  // the rare block that masks, takes the exact max and rescales O and l.
   f32x16 o0 = {}, o1 = {};
-  float m_run = -INFINITY, l_run = 0.f;
-  if (nt > 0) {
-    gload(tile_kp0(0));
-    sstore(0);
-  }
-  __syncthreads();
-  for (int n = 0; n < nt; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < nt) gload(tile_kp0(n + 1));
-    const int kp0 = tile_kp0(n);
-    const int valid = tile_valid(kp0);
-    if (valid > 0) {
-      f32x16 s[NS];
+  float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units (scores * log2(e)/8)
+
+  // scores of one 32-key sub-tile t into s, folding them into the running
+  // tile max mx (raw units)
+  auto scores_t = [&](f32x16& s, float& mx, const u32x4* kt, int t) {
+    const int R = 32 * t + pi_row(l32);
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        s[t] = f32x16{};
-        const int R = 32 * t + pi_row(l32);
+    for (int m = 0; m < 4; ++m) {
+      const bf16x8 kop = as_bf16x8(kt[R * 8 + ((4 * hh + m) ^ swz_k(R))]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], m == 0 ? f32x16{} : s, 0, 0, 0);
+    }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16x8 kop = as_bf16x8(lk[buf][R * 8 + ((4 * hh + m) ^ swz_k(R))]);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], s[t], 0, 0, 0);
-        }
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+  };
+  // exponentials of sub-tile t (against the running max) and its P V product
+  auto exp_pv_t = [&](const f32x16& s, float& ls, const u32x4* vt, int t) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x8 e8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        e8[e] = fast_exp2(fmaf(s[8 * h2 + e], kScaleLog2, -m_run));
+        ls += e8[e];
       }
-      if (valid < KT) {
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-            if (key >= valid) s[t][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = xor32_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2((m_run - m_new) * kScaleLog2);
-      const float mb = m_new * kScaleLog2;
-      float rs = 0.f;
-      bf16x8 pp[NS][2];
+      const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
+      const int ch = 4 * t + 2 * h2 + hh;
+      const bf16x8 v0 = as_bf16x8(vt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
+      const bf16x8 v1 = as_bf16x8(vt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb, o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb, o1, 0, 0, 0);
+    }
+  };
+  // rare block: masking of a partial tile, exact max, rescaling
+  auto rare = [&](f32x16 (&s)[NS], float mx, int valid) {
+    if (valid < KT) {
+      mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          f32x8 e8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = fast_exp2(fmaf(s[t][8 * h2 + e], kScaleLog2, -mb));
-            rs += pv;
-            e8[e] = pv;
-          }
-          pp[t][h2] = __builtin_convertvector(e8, bf16x8);
-        }
-      l_run = l_run * alpha + rs;
-      o0 *= alpha;
-      o1 *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int ch = 4 * t + 2 * h2 + hh;
-          const bf16x8 v0 = as_bf16x8(lv[buf][l32 * VROW + (ch ^ swz_v<KT>(l32))]);
-          const bf16x8 v1 = as_bf16x8(lv[buf][(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pp[t][h2], o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pp[t][h2], o1, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+          if (key >= valid) s[t][r] = -INFINITY;
+          mx = fmaxf(mx, s[t][r]);
         }
     }
-    if (n + 1 < nt) sstore(buf ^ 1);
+    const float m_new = fmaxf(m_run, xor32_max(mx) * kScaleLog2);
+    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+    o0 *= alpha;
+    o1 *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  };
+  auto needs_rare = [&](float mx, int valid) -> bool {
+    // partial tile, or its exact max (both lane halves) more than 64 log2
+    // units above the running max
+    return valid < KT || __any(!(mx * kScaleLog2 - m_run <= kLazySlack));
+  };
+
+  if (nt > 0) {
+    issue_k(tile_kp0(0), 0);
+    issue_v(tile_kp0(0), 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 s[NS];
+  for (int n = 0; n < nt; ++n) {
+    const int slot = n & 1;
+    if (n + 1 < nt) {
+      const int kp1 = tile_kp0(n + 1);
+      issue_k(kp1, slot ^ 1);
+      issue_v(kp1, slot ^ 1);
+    }
+    const u32x4* kt = smem + slot * KCH;
+    const u32x4* vt = smem + (2 + slot) * KCH;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) scores_t(s[t], mx, kt, t);
+    const int valid = tile_valid(tile_kp0(n));
+    if (n == 0 || needs_rare(mx, valid)) rare(s, mx, valid);
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) exp_pv_t(s[t], ls, vt, t);
+    l_run += ls;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32]
   const float l_tot = xor32_sum(l_run);
+  const int qp = qp0 + 32 * w + l32;
   if constexpr (MODE == kSpecialSplit) {
     const int sq = qp - d.np_pad;
     const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
@@ -260,14 +329,16 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       po[(32 + 8 * aa + 4 * hh) / 4] = make_float4(o1[4 * aa], o1[4 * aa + 1], o1[4 * aa + 2], o1[4 * aa + 3]);
     }
     if (hh == 0) {
-      a.part_ml[slot * 2] = m_run;
+      a.part_ml[slot * 2] = m_run / kScaleLog2;  // raw-score units for the reduction
       a.part_ml[slot * 2 + 1] = l_tot;
     }
     return;
   }
+  const int qtok = packed_token(qp, d);
   if (qtok < 0) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? m_run * 0.125f + logf(l_tot) : -INFINITY;
+  // natural-log LSE: (m_run + log2 l) ln 2
+  const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   uint16_t* orow = a.o + ((size_t)h * d.n + qtok) * kHeadDim;
   float* lrow = a.lse + (size_t)h * d.n + qtok;
   float cp = 0.f, cs = inv, lse_out = lse;
@@ -295,7 +366,6 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         x[2] += cp * __uint_as_float(old[1] << 16);
         x[3] += cp * __uint_as_float(old[1] & 0xffff0000u);
       }
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       *dst = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
     }
   };
@@ -389,6 +459,7 @@ static hipError_t run_attn(const AttnArgs& a, hipStream_t st) {
   attn_kernel<KT, MODE><<<xcd_grid(a.n_items), 2 * KT, 0, st>>>(a);
   return hipGetLastError();
 }
+
 
 static AttnArgs base_args(const Dims& d, const uint16_t* q, const uint16_t* kp,
                           const uint16_t* vt, uint16_t* o, float* lse) {
