@@ -34,13 +34,61 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="layer shape index 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense comparison and the tau=0 diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (torch.neg into a second "
+                         "buffer) 5 times and exit: the reference reading for HBM counters")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "attn_patch_rows_32f_hbm_traffic.txt")
+KERNEL_SOURCES = ("attention.hip", "bsga_internal.hpp")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_global_bsga_amd",
+                        "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the patch-row kernel from the committed counter
+    summary, or None when that summary was taken on different kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.strip()
+        if fields.get("kernel_source_sha256") != kernel_source_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda:0").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 2, "bytes_written": n * 2,
+                      "launches": 5}), flush=True)
 
 
 def computed_entries(row_ptr, col_idx, n_patch, block, heads, n_special):
@@ -103,6 +151,9 @@ def main():
               "sharding across GPUs is described in the design notes but not built.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from block_sparse_global_bsga_amd import bsga, synth
 
@@ -126,24 +177,31 @@ def main():
     kv = torch.empty(bsga.packed_kv_bytes(shape) + 256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    stages = ("predict_mask", "select", "pack_kv", "patch_rows", "special_rows")
+
     def step(rho, tau, ev=None):
+        mark = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        mark(0)
         bsga.predict_mask(shape, q, k, probs=probs, ws=ws_pred)
+        mark(1)
         bsga.select(shape, probs, rho, tau, x.rho_per_head, row_ptr=row_ptr, col_idx=col_idx,
                     ws=ws_sel)
+        mark(2)
         bsga.pack_kv(shape, k, v, kv=kv)
-        if ev is not None:
-            ev[0].record(stream)
+        mark(3)
         bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
-        if ev is not None:
-            ev[1].record(stream)
+        mark(4)
         bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
+        mark(5)
 
-    def timed(fn, steps, warmup, with_kernel_events=False):
+    def timed(fn, steps, warmup, with_stage_events=False):
+        """Average ms per step over `steps` timed steps, plus (optionally) the
+        average ms of each stage from HIP events recorded on the launch stream."""
         for _ in range(warmup):
             fn(None)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)] if with_kernel_events else [None] * steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+               for _ in range(steps)] if with_stage_events else [None] * steps
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
@@ -152,12 +210,16 @@ def main():
         stop.record(stream)
         torch.cuda.synchronize()
         total = start.elapsed_time(stop) / steps
-        kern = (sum(a.elapsed_time(b) for a, b in evs) / steps) if with_kernel_events else None
-        return total, kern
+        per = None
+        if with_stage_events:
+            per = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+                   for j, name in enumerate(stages)}
+        return total, per
 
     print(f"# warmup {args.warmup} + {args.steps} timed layer steps, {cfg.name}", file=sys.stderr,
           flush=True)
-    ms, kern_ms = timed(lambda ev: step(cfg.rho, cfg.tau, ev), args.steps, args.warmup, True)
+    ms, stage_ms = timed(lambda ev: step(cfg.rho, cfg.tau, ev), args.steps, args.warmup, True)
+    kern_ms = stage_ms["patch_rows"]
     rp = row_ptr.cpu().numpy()
     ci = col_idx[:int(rp[-1])].cpu().numpy()
     pp, sp = computed_entries(rp, ci, cfg.n_patch, cfg.block, cfg.heads, cfg.n_special)
@@ -181,7 +243,8 @@ def main():
         layer_call_ms, _ = timed(lambda _ev: bsga.layer(shape, q, k, v, cfg.rho, cfg.tau,
                                                         x.rho_per_head, bufs=bufs),
                                  args.steps, 2)
-        ms0, kern0 = timed(lambda ev: step(cfg.rho, 0.0, ev), max(3, args.steps // 2), 2, True)
+        ms0, st0 = timed(lambda ev: step(cfg.rho, 0.0, ev), max(3, args.steps // 2), 2, True)
+        kern0 = st0["patch_rows"]
         rp0 = row_ptr.cpu().numpy()
         pp0, sp0 = computed_entries(rp0, col_idx[:int(rp0[-1])].cpu().numpy(), cfg.n_patch,
                                     cfg.block, cfg.heads, cfg.n_special)
@@ -199,6 +262,25 @@ def main():
                               4 * HEAD_DIM * (pp0 + cfg.heads * cfg.n_patch * cfg.n_special)
                               / (kern0 * 1e-3) / 1e12, 1)},
         }
+
+    # algorithmic HBM bytes of the bandwidth-bound stages (bf16 = 2 bytes)
+    nnz = int(rp[-1])
+    tok_bytes = cfg.heads * HEAD_DIM * 2
+    stage_bytes = {
+        "predict_mask": 2 * cfg.n_patch * tok_bytes + cfg.heads * B * B * 4,
+        "select": cfg.heads * B * B * 4 + (cfg.heads * B + 1 + nnz) * 4,
+        "pack_kv": 4 * n * tok_bytes,
+    }
+    stages_out = {}
+    for name, t in stage_ms.items():
+        e = {"ms": round(t, 4)}
+        if name in stage_bytes:
+            e["algorithmic_bytes"] = stage_bytes[name]
+            e["GB/s"] = round(stage_bytes[name] / (t * 1e-3) / 1e9, 1)
+        stages_out[name] = e
+    stages_out["special_rows"]["TFLOP/s"] = round(
+        4 * HEAD_DIM * cfg.heads * cfg.n_special * n / (stage_ms["special_rows"] * 1e-3) / 1e12, 1)
+    stages_out["patch_rows"]["TFLOP/s"] = round(kern_tflops, 1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -228,7 +310,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_kernel<128, sparse+special keys>",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-                     "kernel_ms": round(kern_ms, 4), "traffic": None},
+                     "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic()},
+        "stages": stages_out,
         "cpu_baseline": cpu,
         **extras,
     }
