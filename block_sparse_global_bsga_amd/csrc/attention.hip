@@ -147,11 +147,29 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     tile0 = d.np_pad / KT;
     nt = d.ns_pad / KT;
   }
-  auto tile_kp0 = [&](int n) -> int {
+  // everything above is wave-uniform; keep it in scalar registers
+  h = __builtin_amdgcn_readfirstlane(h);
+  qp0 = __builtin_amdgcn_readfirstlane(qp0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
+  tile0 = __builtin_amdgcn_readfirstlane(tile0);
+  // Position of tile n, in two steps so that the global load of a CSR entry
+  // can be issued long before its value is consumed: tile_raw(n) loads the
+  // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
+  // it into the tile's first packed key.
+  auto tile_raw = [&](int n) -> int {
+    if constexpr (MODE == kSparse || MODE == kSparseFused) {
+      return nt_csr > 0 ? cols[min(n, nt_csr - 1)] : 0;
+    } else {
+      return 0;
+    }
+  };
+  auto tile_kp0 = [&](int n, int raw) -> int {
+    raw = __builtin_amdgcn_readfirstlane(raw);
     if constexpr (MODE == kSparse) {
-      return min(max(cols[n], 0), d.B - 1) * KT;
+      return min(max(raw, 0), d.B - 1) * KT;
     } else if constexpr (MODE == kSparseFused) {
-      return n < nt_csr ? min(max(cols[n], 0), d.B - 1) * KT : d.np_pad + (n - nt_csr) * KT;
+      return n < nt_csr ? min(max(raw, 0), d.B - 1) * KT : d.np_pad + (n - nt_csr) * KT;
     } else {
       return (tile0 + n) * KT;
     }
@@ -287,9 +305,15 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     return valid < KT || __any(!(mx * kScaleLog2 - m_run <= kLazySlack));
   };
 
+  // CSR entries run two tiles ahead of the compute: the entry of tile n+2 is
+  // loaded during iteration n and consumed after that iteration's closing
+  // wait, so no wait in the middle of an iteration (which would also stall on
+  // the tile prefetch) is needed.
+  int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
   if (nt > 0) {
-    issue_k(tile_kp0(0), 0);
-    issue_v(tile_kp0(0), 0);
+    const int kp0 = tile_kp0(0, raw_cur);
+    issue_k(kp0, 0);
+    issue_v(kp0, 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -297,16 +321,17 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   for (int n = 0; n < nt; ++n) {
     const int slot = n & 1;
     if (n + 1 < nt) {
-      const int kp1 = tile_kp0(n + 1);
+      const int kp1 = tile_kp0(n + 1, raw_nxt);
       issue_k(kp1, slot ^ 1);
       issue_v(kp1, slot ^ 1);
     }
+    const int raw_after = tile_raw(n + 2);
     const u32x4* kt = smem + slot * KCH;
     const u32x4* vt = smem + (2 + slot) * KCH;
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NS; ++t) scores_t(s[t], mx, kt, t);
-    const int valid = tile_valid(tile_kp0(n));
+    const int valid = tile_valid(tile_kp0(n, raw_cur));
     if (n == 0 || needs_rare(mx, valid)) rare(s, mx, valid);
     float ls = 0.f;
 #pragma unroll
@@ -314,6 +339,8 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     l_run += ls;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    raw_cur = raw_nxt;
+    raw_nxt = raw_after;
   }
 
   // o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32]
