@@ -104,12 +104,20 @@ __device__ inline int swz_v(int d) {
   else return ((d >> 1) & 7) ^ ((d & 1) << 2);
 }
 
-template <int KT, int MODE>
-__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
+// QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
+// per SIMD targeted (bounds the registers of a wave to 512 / WPE).
+template <int QT, int KT, int MODE, int WPE>
+__global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_kernel(
     AttnArgs a) {
+  constexpr int NW = QT / 32;       // waves
   constexpr int NS = KT / 32;       // 32-key sub-tiles
   constexpr int VROW = KT / 8;      // 16-byte chunks per V^T row
   constexpr int KCH = 8 * KT;       // chunks of a K tile (= chunks of a V^T tile)
+  constexpr int LPW = KCH / (64 * NW);  // 64-chunk loads per wave per K (and V^T) tile
+  // patch blocks are one query tile; a kept block spans TPB key tiles
+  constexpr int TPB = QT / KT;
+  static_assert(LPW >= 2 && LPW % 2 == 0 && (KT == 64 || LPW % 4 == 0), "tile loads");
+  static_assert(TPB >= 1 && QT % KT == 0, "tile shape");
   __shared__ u32x4 smem[4 * KCH];   // K slots 0, 1 then V^T slots 0, 1
 
   const Dims& d = a.d;
@@ -123,14 +131,14 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int32_t* cols = nullptr;
   if constexpr (MODE == kSparse || MODE == kSparseFused) {
     h = item / d.B;
-    qp0 = (item - h * d.B) * KT;
+    qp0 = (item - h * d.B) * QT;
     const int r0 = a.row_ptr[item];
     cols = a.col_idx + r0;
     nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
-    nt = nt_csr + (MODE == kSparseFused ? d.ns_pad / KT : 0);
+    nt = nt_csr * TPB + (MODE == kSparseFused ? d.ns_pad / KT : 0);
   } else if constexpr (MODE == kDense) {
     h = item / a.q_tiles;
-    qp0 = (item - h * a.q_tiles) * KT;
+    qp0 = (item - h * a.q_tiles) * QT;
     nt = d.ntot_pad / KT;
   } else if constexpr (MODE == kSpecialSplit) {
     const int per_h = a.q_tiles * a.nsplit;
@@ -138,12 +146,12 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int rem = item - h * per_h;
     const int qt = rem / a.nsplit;
     split = rem - qt * a.nsplit;
-    qp0 = d.np_pad + qt * KT;
+    qp0 = d.np_pad + qt * QT;
     tile0 = split * a.tiles_per_split;
     nt = max(0, min(a.tiles_per_split, d.ntot_pad / KT - tile0));
   } else {
     h = item / a.q_tiles;
-    qp0 = (item - h * a.q_tiles) * KT;
+    qp0 = (item - h * a.q_tiles) * QT;
     tile0 = d.np_pad / KT;
     nt = d.ns_pad / KT;
   }
@@ -156,20 +164,21 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // Position of tile n, in two steps so that the global load of a CSR entry
   // can be issued long before its value is consumed: tile_raw(n) loads the
   // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
-  // it into the tile's first packed key.
+  // it into the tile's first packed key.  Kept block j of the row covers tiles
+  // j TPB .. j TPB + TPB - 1.
   auto tile_raw = [&](int n) -> int {
     if constexpr (MODE == kSparse || MODE == kSparseFused) {
-      return nt_csr > 0 ? cols[min(n, nt_csr - 1)] : 0;
+      return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0;
     } else {
       return 0;
     }
   };
   auto tile_kp0 = [&](int n, int raw) -> int {
     raw = __builtin_amdgcn_readfirstlane(raw);
-    if constexpr (MODE == kSparse) {
-      return min(max(raw, 0), d.B - 1) * KT;
-    } else if constexpr (MODE == kSparseFused) {
-      return n < nt_csr ? min(max(raw, 0), d.B - 1) * KT : d.np_pad + (n - nt_csr) * KT;
+    if constexpr (MODE == kSparse || MODE == kSparseFused) {
+      const int nb = nt_csr * TPB;
+      if (MODE == kSparseFused && n >= nb) return d.np_pad + (n - nb) * KT;
+      return min(max(raw, 0), d.B - 1) * QT + (n % TPB) * KT;
     } else {
       return (tile0 + n) * KT;
     }
@@ -193,8 +202,8 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 
   // ---- direct-to-LDS tile loads into two rings (K rows, V^T rows), two
-  // slots each.  Every wave issues 4 loads of 64 x 16 B per K tile and 4 per
-  // V^T tile; load i of wave w fills chunks (4w + i) * 64 + lane of the tile.
+  // slots each.  Every wave issues LPW loads of 64 x 16 B per K tile and LPW
+  // per V^T tile; load i of wave w fills chunks (LPW w + i) * 64 + lane.
   // The swizzle of the row a lane fills depends on i only through i mod 2
   // (K, and V^T of 64-key tiles) or i mod 4 (V^T of 128-key tiles), so a few
   // per-lane byte offsets cover all loads.  Addresses are a uniform base
@@ -219,20 +228,20 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   auto issue_k = [&](int kp0, int slot) {
-    lds_u32x4* dst = (lds_u32x4*)&smem[slot * KCH + w * 256];
+    lds_u32x4* dst = (lds_u32x4*)&smem[slot * KCH + w * LPW * 64];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * w + i;  // 64-chunk block of the K tile: rows 8 blk .. 8 blk + 7
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = LPW * w + i;  // 64-chunk block of the K tile: rows 8 blk .. 8 blk + 7
       __builtin_amdgcn_global_load_lds(
           (const void*)(kbase + (size_t)(kp0 + 8 * blk) * 128 + koff[i & 1]),
           (__attribute__((address_space(3))) void*)(dst + i * 64), 16, 0, 0);
     }
   };
   auto issue_v = [&](int kp0, int slot) {
-    lds_u32x4* dst = (lds_u32x4*)&smem[(2 + slot) * KCH + w * 256];
+    lds_u32x4* dst = (lds_u32x4*)&smem[(2 + slot) * KCH + w * LPW * 64];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * w + i;
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = LPW * w + i;
       const size_t row0 = KT == 128 ? 4 * blk : 8 * blk;  // first V^T row of the block
       __builtin_amdgcn_global_load_lds(
           (const void*)(vbase + row0 * vrow_bytes + (size_t)kp0 * 2 + voff[i & 3]),
@@ -259,7 +268,8 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], m == 0 ? f32x16{} : s, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    // a plain chain: the backend folds it into one v_max3 per two scores
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
   };
   // exponentials of sub-tile t (against the running max) and its P V product
   auto exp_pv_t = [&](const f32x16& s, float& ls, const u32x4* vt, int t) {
@@ -334,8 +344,13 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int valid = tile_valid(tile_kp0(n, raw_cur));
     if (n == 0 || needs_rare(mx, valid)) rare(s, mx, valid);
     float ls = 0.f;
+    // the exponential / P V stretch runs at raised issue priority, so that a
+    // wave in it keeps the SIMD's other wave (typically in its score MFMAs)
+    // from starving the VALU
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < NS; ++t) exp_pv_t(s[t], ls, vt, t);
+    __builtin_amdgcn_s_setprio(0);
     l_run += ls;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -481,9 +496,9 @@ hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint
   return hipGetLastError();
 }
 
-template <int KT, int MODE>
+template <int QT, int KT, int MODE, int WPE = 2>
 static hipError_t run_attn(const AttnArgs& a, hipStream_t st) {
-  attn_kernel<KT, MODE><<<xcd_grid(a.n_items), 2 * KT, 0, st>>>(a);
+  attn_kernel<QT, KT, MODE, WPE><<<xcd_grid(a.n_items), 2 * QT, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -507,7 +522,7 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
-  return d.b == 64 ? run_attn<64, kSparse>(a, st) : run_attn<128, kSparse>(a, st);
+  return d.b == 64 ? run_attn<64, 64, kSparse>(a, st) : run_attn<128, 128, kSparse>(a, st);
 }
 
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
@@ -517,7 +532,7 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
-  return d.b == 64 ? run_attn<64, kSparseFused>(a, st) : run_attn<128, kSparseFused>(a, st);
+  return d.b == 64 ? run_attn<64, 64, kSparseFused>(a, st) : run_attn<128, 128, kSparseFused>(a, st);
 }
 
 struct SplitPlan {
@@ -554,7 +569,7 @@ hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t*
   a.nsplit = p.nsplit;
   a.tiles_per_split = p.tps;
   a.n_items = d.H * p.q_tiles * p.nsplit;
-  hipError_t e = run_attn<128, kSpecialSplit>(a, st);
+  hipError_t e = run_attn<128, 128, kSpecialSplit>(a, st);
   if (e != hipSuccess) return e;
   const int items = d.H * d.ns;
   special_reduce_kernel<<<(items + 3) / 4, 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d, p.nsplit);
@@ -569,7 +584,7 @@ hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
   AttnArgs b = base_args(d, q, kp, vt, o, lse);
   b.q_tiles = d.np_pad / 128;
   b.n_items = d.H * b.q_tiles;
-  return run_attn<128, kPatchSpecial>(b, st);
+  return run_attn<128, 128, kPatchSpecial>(b, st);
 }
 
 hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
@@ -577,7 +592,7 @@ hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* kp, co
   AttnArgs a = base_args(d, q, kp, vt, o, lse);
   a.q_tiles = d.ntot_pad / 128;
   a.n_items = d.H * a.q_tiles;
-  return run_attn<128, kDense>(a, st);
+  return run_attn<128, 128, kDense>(a, st);
 }
 
 }  // namespace bsga
