@@ -307,7 +307,8 @@ def main():
                    "tau": cfg.tau, "parallelism": "none (1 GPU)"},
         "layer_frac_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "density": round(density, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128, sparse+special keys>",
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_kernel<128, 128, kSparseFused> (bsga_patch_rows_packed)",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic()},

@@ -5,7 +5,7 @@
 // log-sum-exp merge (key design 3 and the framework flowchart), and the dense
 // path (equation "Attention") used for comparison.
 //
-// One tile core serves every mode.  A workgroup of KT/32 waves owns KT query
+// One tile core serves every mode.  A workgroup of QT/32 waves owns QT query
 // rows (32 per wave) and walks a list of KT-key tiles: the kept blocks of its
 // CSR row (sparse), every tile (dense), a range of tiles (split-K for the
 // special queries) or the special-token tiles (patch queries x special keys).
@@ -23,21 +23,20 @@
 // pi(i) (bits 2 and 3 of i swapped) into A row i makes them the keys
 // 16m + 8hh + e, e = 0..7, i.e. contiguous.
 //
-// Instruction budget.  On gfx950 an exp2 costs about four FMAs, and every
-// score needs one exp2 and one FMA, so the softmax is kept to that minimum:
+// Instruction budget.  On gfx950 an exp2 costs about three FMAs of issue
+// time, and every score needs one exp2, one FMA and one add, so the softmax
+// is kept to that minimum:
 //  * lazy running max: a tile is exponentiated against the running max
 //    directly (no rescaling of O) unless its exact max lies more than 64 log2
-//    units above it; that max comes from a v_max3 chain folded into the
-//    score computation;
+//    units above it; that max is one v_max3 chain over the tile's scores;
 //  * the rare block (first tile, partial tile, or such a jump) masks keys
 //    past a partial block, takes the exact max and rescales O and l; full
 //    tiles never execute any masking instructions;
 //  * the first product of each score accumulator starts from the constant 0.
-// The tile loop is software-pipelined: iteration n produces the scores of
-// tile n+1 sub-tile by sub-tile next to tile n's exponentials and P V
-// products, so the MFMA pipe always has independent work beside the softmax
-// arithmetic.  K and V^T have separate two-slot LDS rings (K is fetched two
-// tiles ahead, V^T one tile ahead), one barrier per tile.
+// Per tile a wave computes all scores, then exponentiates and multiplies by V
+// one 32-key sub-tile at a time (the exponentials of one sub-tile run beside
+// the P V products of the previous one).  The next tile's K and V^T are in
+// flight meanwhile: two LDS slots each, one barrier per tile.
 //
 // K and V are first packed (once per layer) into "packed order": patch
 // tokens, padding, special tokens, padding (each segment a multiple of 128),
@@ -45,8 +44,8 @@
 // reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at
 // base + 16 * lane: no staging registers, no LDS store instructions); the
 // bank swizzle is applied on the global side, the lane that fills LDS chunk
-// (row, physical chunk pc) fetching logical chunk pc ^ swizzle(row).  Half
-// the waves fetch K rows, the other half V^T rows, one tile ahead.
+// (row, physical chunk pc) fetching logical chunk pc ^ swizzle(row).  Every
+// wave fetches its share of both the K and the V^T tile.
 #include <type_traits>
 
 #include "bsga_internal.hpp"
@@ -249,12 +248,10 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     }
   };
 
-  // ---- software-pipelined tile loop.  Iteration n exponentiates tile n and
-  // accumulates its P V while the scores of tile n+1 are produced, so the
-  // MFMA pipe always has independent work next to the softmax arithmetic.
-  // Before a tile's exponentials, a uniform flag (partial tile, first tile,
-  // or its exact max more than 64 log2 units above the running max) selects
-  // the rare block that masks, takes the exact max and rescales O and l.
+  // ---- tile loop.  Before a tile's exponentials, a uniform flag (partial
+  // tile, first tile, or its exact max more than 64 log2 units above the
+  // running max) selects the rare block that masks, takes the exact max and
+  // rescales O and l.
   f32x16 o0 = {}, o1 = {};
   float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units (scores * log2(e)/8)
 
