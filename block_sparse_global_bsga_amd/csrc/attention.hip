@@ -264,12 +264,23 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       const bf16x8 kop = as_bf16x8(kt[R * 8 + ((4 * hh + m) ^ swz_k(R))]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], m == 0 ? f32x16{} : s, 0, 0, 0);
     }
-#pragma unroll
     // a plain chain: the backend folds it into one v_max3 per two scores
+#pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
   };
-  // exponentials of sub-tile t (against the running max) and its P V product
+  // exponentials of sub-tile t (against the running max) and its P V product.
+  // The sub-tile's four V^T operands are read first and the scheduler may not
+  // sink them (sched_barrier), so the LDS latency hides behind the 16
+  // exponentials instead of stalling each MFMA.
   auto exp_pv_t = [&](const f32x16& s, float& ls, const u32x4* vt, int t) {
+    bf16x8 va[2], vb[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int ch = 4 * t + 2 * h2 + hh;
+      va[h2] = as_bf16x8(vt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
+      vb[h2] = as_bf16x8(vt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       f32x8 e8;
@@ -279,11 +290,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         ls += e8[e];
       }
       const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
-      const int ch = 4 * t + 2 * h2 + hh;
-      const bf16x8 v0 = as_bf16x8(vt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
-      const bf16x8 v1 = as_bf16x8(vt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb, o1, 0, 0, 0);
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pb, o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pb, o1, 0, 0, 0);
     }
   };
   // rare block: masking of a partial tile, exact max, rescaling
