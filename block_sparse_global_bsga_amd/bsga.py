@@ -37,7 +37,7 @@ EXPORTS = [
     "bsga_select", "bsga_sparse_attn", "bsga_special_dense", "bsga_dense_attn",
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
-    "bsga_special_rows_packed",
+    "bsga_special_rows_packed", "bsga_redistribute",
 ]
 
 
@@ -55,6 +55,8 @@ _lib.bsga_status_string.argtypes = [ctypes.c_int]
 _lib.bsga_num_blocks.argtypes = [_sp, ctypes.POINTER(ctypes.c_int32)]
 _lib.bsga_keep_count.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
 _lib.bsga_csr_capacity.argtypes = [_sp, ctypes.POINTER(ctypes.c_int64)]
+_lib.bsga_redistribute.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.c_double,
+                                   ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
 _lib.bsga_workspace_bytes.argtypes = [_sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
 _lib.bsga_predict_mask.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
@@ -122,6 +124,16 @@ def keep_count(n_blocks: int, rho: float) -> int:
     out = ctypes.c_int32()
     _check(_lib.bsga_keep_count(n_blocks, rho, ctypes.byref(out)), "bsga_keep_count")
     return out.value
+
+
+def redistribute(weights: Sequence[float], mean_rho: float, rho_min: float,
+                 rho_max: float) -> list:
+    """Per-head rho from head weights (bsga_redistribute, host-side)."""
+    h = len(weights)
+    w = (ctypes.c_double * h)(*[float(x) for x in weights])
+    out = (ctypes.c_double * h)()
+    _check(_lib.bsga_redistribute(h, w, mean_rho, rho_min, rho_max, out), "bsga_redistribute")
+    return list(out)
 
 
 def csr_capacity(shape: LayerShape) -> int:

@@ -97,6 +97,24 @@ int bsga_num_blocks(const bsga_shape* shape, int32_t* n_blocks);
  * 214.  rho must lie in [0, 1]. */
 int bsga_keep_count(int32_t n_blocks, double rho, int32_t* k);
 
+/* Head-wise budget redistribution ([HeSS] proposed method: the layer's total
+ * attention budget is reallocated across heads by iterative capping, denser
+ * attention for more sensitive heads).  With keep fractions
+ * kappa_h = 1 - rho_h, the result is the unique solution of
+ *   kappa_h = clamp(lambda * weights[h], 1 - rho_max, 1 - rho_min),
+ *   mean_h kappa_h = 1 - mean_rho,
+ * i.e. keep fractions proportional to the weights, clipped at both bounds,
+ * with the budget a clipped head cannot take spread over the others.
+ *   weights: HOST array of `heads` finite values > 0 (e.g. per-head
+ *     sensitivity scores; they are not computed here).
+ *   0 <= rho_min <= mean_rho <= rho_max <= 1; 1 <= heads <= BSGA_MAX_HEADS.
+ *   rho_out: HOST array of `heads` values, the per-head rho for bsga_select.
+ * Host-only computation (no GPU work, no allocation); O(heads log heads).
+ * Returns BSGA_ERR_INVALID_ARG for null pointers, a bad count, a weight that
+ * is not finite and positive, or bounds out of order. */
+int bsga_redistribute(int32_t heads, const double* weights, double mean_rho,
+                      double rho_min, double rho_max, double* rho_out);
+
 /* Entries col_idx must be able to hold: H * B * B (every block kept). */
 int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries);
 

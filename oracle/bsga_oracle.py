@@ -44,7 +44,10 @@ design document):
 * the last patch block may be partial; its mean is over its valid tokens;
 * special tokens: 5 per frame, first in each frame; special queries attend to
   every token; patch queries attend to every special token plus the patch
-  tokens of their kept blocks, all in one softmax.
+  tokens of their kept blocks, all in one softmax;
+* head-wise budgets ([HeSS], iterative capping, no formula given): keep
+  fractions 1 - rho_h proportional to positive per-head weights, clipped to
+  [1 - rho_max, 1 - rho_min], with their mean fixed at 1 - mean_rho.
 """
 from __future__ import annotations
 
@@ -264,3 +267,39 @@ def computed_entries(frames: int, patches_per_frame: int,
             pp += int(size[i]) * int(size[np.asarray(cols, dtype=np.int64)].sum())
     ns = heads * (n_s * (n_p + n_s) + n_p * n_s)
     return pp, ns
+
+
+# ----------------------------------------------------------------------------
+# head-wise budget redistribution  ([HeSS] proposed method)
+# ----------------------------------------------------------------------------
+def redistribute_budget(weights: Sequence[float], mean_rho: float, rho_min: float,
+                        rho_max: float) -> List[float]:
+    """Per-head rho from per-head weights: keep fractions kappa_h = 1 - rho_h
+    proportional to the weights, clipped to [1 - rho_max, 1 - rho_min], with
+    mean kappa_h = 1 - mean_rho (the budget a clipped head cannot take goes to
+    the others).
+
+    Solved exactly in rational arithmetic: the clipped total
+    f(lam) = sum_h clamp(lam w_h, lo, hi) is piecewise linear in lam with
+    breakpoints lo / w_h and hi / w_h; the segment containing the target is
+    found among the sorted breakpoints and solved linearly."""
+    from fractions import Fraction
+    w = [Fraction(float(x)) for x in weights]
+    lo, hi = 1 - Fraction(float(rho_max)), 1 - Fraction(float(rho_min))
+    target = len(w) * (1 - Fraction(float(mean_rho)))
+    if hi == lo:
+        return [float(mean_rho)] * len(w)
+
+    def clipped_total(lam):
+        return sum(min(max(lam * x, lo), hi) for x in w)
+
+    points = sorted(set([lo / x for x in w] + [hi / x for x in w]))
+    lam = points[-1]
+    if target <= clipped_total(points[0]):
+        lam = points[0]
+    for a, b in zip(points, points[1:]):
+        fa, fb = clipped_total(a), clipped_total(b)
+        if fa <= target <= fb:
+            lam = a if fb == fa else a + (target - fa) * (b - a) / (fb - fa)
+            break
+    return [float(1 - min(max(lam * x, lo), hi)) for x in w]

@@ -393,4 +393,49 @@ def pin_computed_entries(O):
     assert pp + ns == H * N * N and pp == H * n_p * n_p
 
 
+def pin_budget_golden(O):
+    """[HeSS] proposed method: hand-worked redistributions (one head capped
+    high, one clipped low, both bounds active, equal weights)."""
+    from fractions import Fraction
+    g = _golden("budget_worked.json")
+    for c in g["cases"]:
+        got = O.redistribute_budget(c["weights"], c["mean_rho"], c["rho_min"], c["rho_max"])
+        want = [float(Fraction(x)) for x in c["rho"]]
+        assert np.allclose(got, want, rtol=0, atol=1e-15), (c["note"], got, want)
+
+
+def pin_budget_invariants(O):
+    """Mean preserved, bounds respected, heavier heads never sparser, scale
+    invariance in the weights, no clipping -> exactly proportional; checked
+    against a float64 bisection of the defining equation on random cases."""
+    rng = np.random.default_rng(17)
+    for trial in range(150):
+        H = int(rng.integers(1, 24))
+        w = np.exp(rng.normal(0.0, 1.5, size=H))
+        lo_r, hi_r = sorted(rng.uniform(0.0, 1.0, size=2))
+        mean = float(rng.uniform(lo_r, hi_r))
+        rho = np.array(O.redistribute_budget(w, mean, lo_r, hi_r))
+        assert abs(rho.mean() - mean) < 1e-12, trial
+        assert np.all(rho >= lo_r - 1e-15) and np.all(rho <= hi_r + 1e-15)
+        order = np.argsort(w)
+        assert np.all(np.diff(rho[order]) <= 1e-15)
+        rho2 = np.array(O.redistribute_budget(w * 7.25, mean, lo_r, hi_r))
+        assert np.allclose(rho, rho2, atol=1e-15)
+        # independent solve: bisection on lambda of sum clamp(lam w) = H (1 - mean)
+        lo, hi, tot = 1 - hi_r, 1 - lo_r, H * (1 - mean)
+        a, b = lo / w.max(), hi / w.min()
+        for _ in range(200):
+            m = 0.5 * (a + b)
+            if np.clip(m * w, lo, hi).sum() < tot:
+                a = m
+            else:
+                b = m
+        ref = 1 - np.clip(0.5 * (a + b) * w, lo, hi)
+        assert np.allclose(rho, ref, atol=1e-9), trial
+    # wide bounds: plain proportional split
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    rho = O.redistribute_budget(w, 0.75, 0.0, 1.0)
+    assert np.allclose(1 - np.array(rho), 4 * 0.25 * w / w.sum(), atol=1e-15)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

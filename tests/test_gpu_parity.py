@@ -140,6 +140,30 @@ def test_select_bitexact(lib, name, param):
     assert np.array_equal(ci, ref_ci), (name, param)
 
 
+@pytest.mark.parametrize("tau", [0.0, 0.9])
+def test_select_with_redistributed_budgets(lib, tau):
+    """Per-head rho from bsga_redistribute (weights spread over 1..13, mean
+    0.8, rho in [0.5, 0.95]) through bsga_select; the reference selects with
+    the oracle's own redistribution of the same weights."""
+    import torch
+    from gpu_helpers import layer_shape, say
+    x = inputs("vggt-32f")
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    weights = [1.0 + (h * 7919) % 13 for h in range(cfg.heads)]
+    rho_h = lib.redistribute(weights, 0.8, 0.5, 0.95)
+    rho_ref = O.redistribute_budget(weights, 0.8, 0.5, 0.95)
+    say(f"[select-redistributed] tau={tau} rho_h={[round(r, 4) for r in rho_h]}")
+    q, k, _ = _upload(x)
+    probs = lib.predict_mask(shape, q, k)
+    row_ptr, col_idx = lib.select(shape, probs, cfg.rho, tau, rho_h)
+    torch.cuda.synchronize()
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy()[:rp[-1]]
+    ref_rp, ref_ci = O.select_blocks(probs.cpu().numpy(), tau, cfg.rho, rho_ref)
+    assert np.array_equal(rp, ref_rp) and np.array_equal(ci, ref_ci)
+
+
 def test_select_ties_and_flat_rows(lib):
     """Uniform rows and rows with many exact ties, uploaded directly."""
     import torch

@@ -183,11 +183,45 @@ def _entries_ignore_partial(O):
     O.computed_entries = f
 
 
+def _budget_one_sided(O):
+    # a single pass of upper capping, then a clip at the lower bound without
+    # re-solving (the budget no longer adds up, or a head stays capped wrongly)
+    def f(weights, mean_rho, rho_min, rho_max):
+        w = np.asarray(weights, dtype=np.float64)
+        lo, hi, tot = 1 - rho_max, 1 - rho_min, len(w) * (1 - mean_rho)
+        kappa = np.full(len(w), np.nan)
+        free = np.ones(len(w), dtype=bool)
+        while True:
+            lam = (tot - np.nansum(np.where(free, 0, kappa))) / w[free].sum()
+            over = free & (lam * w > hi)
+            if not over.any():
+                break
+            kappa[over] = hi
+            free &= ~over
+        kappa[free] = np.maximum(lam * w[free], lo)
+        return list(1 - kappa)
+    O.redistribute_budget = f
+
+
+def _budget_unclipped(O):
+    def f(weights, mean_rho, rho_min, rho_max):
+        w = np.asarray(weights, dtype=np.float64)
+        return list(1 - len(w) * (1 - mean_rho) * w / w.sum())
+    O.redistribute_budget = f
+
+
+def _budget_inverse(O):
+    # denser attention for the less sensitive heads
+    real = O.redistribute_budget
+    O.redistribute_budget = lambda w, *a: real([1.0 / x for x in w], *a)
+
+
 MUTANTS = [_no_scale, _transposed_scores, _softmax_wrong_axis, _ascending_rank,
            _tie_high_index, _strict_coverage, _coverage_off_by_one,
            _min_not_max, _ceil_keep, _binary_float_keep, _pool_divides_by_b,
            _specials_last, _attn_no_scale, _lse_no_max, _masked_as_zero_logit,
-           _no_special_keys, _special_queries_sparse, _entries_ignore_partial]
+           _no_special_keys, _special_queries_sparse, _entries_ignore_partial,
+           _budget_one_sided, _budget_unclipped, _budget_inverse]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
