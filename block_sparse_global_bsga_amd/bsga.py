@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 (OP_PREDICT_MASK, OP_SELECT, OP_SPARSE_ATTN, OP_SPECIAL_DENSE, OP_DENSE_ATTN, OP_LAYER,
- OP_SPECIAL_DENSE_PACKED) = range(7)
+ OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT) = range(8)
 MAX_HEADS = 256
 MAX_BLOCKS = 4096
 
@@ -37,7 +37,7 @@ EXPORTS = [
     "bsga_select", "bsga_sparse_attn", "bsga_special_dense", "bsga_dense_attn",
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
-    "bsga_special_rows_packed", "bsga_redistribute",
+    "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select",
 ]
 
 
@@ -61,6 +61,8 @@ _lib.bsga_workspace_bytes.argtypes = [_sp, ctypes.c_int, ctypes.POINTER(ctypes.c
 _lib.bsga_predict_mask.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
                              ctypes.c_int64, _p, ctypes.c_size_t, _p]
+_lib.bsga_probe_select.argtypes = [_sp, _p, _p, ctypes.c_int32, _p, _p, _p, ctypes.c_int64, _p,
+                                   ctypes.c_size_t, _p]
 _lib.bsga_sparse_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_special_dense.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_dense_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -234,6 +236,28 @@ def select(shape: LayerShape, probs: torch.Tensor, rho: float, tau: float,
                             _ws_len(ws), _stream(dev)), "bsga_select")
     del keep
     return row_ptr, col_idx
+
+
+def probe_select(shape: LayerShape, q: torch.Tensor, k: torch.Tensor, topk: int, *,
+                 want_scores: bool = False, row_ptr: Optional[torch.Tensor] = None,
+                 col_idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Query-probe Top-K block lists.  Returns (row_ptr, col_idx) or, with
+    want_scores, (row_ptr, col_idx, scores [H][N_p] float32)."""
+    q, k = _bf16(q, "q", shape), _bf16(k, "k", shape)
+    dev = q.device
+    B = num_blocks(shape)
+    n_p = shape.frames * shape.patches_per_frame
+    if row_ptr is None:
+        row_ptr = torch.empty(shape.heads * B + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(csr_capacity(shape), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(shape, OP_PROBE_SELECT, dev)
+    scores = torch.empty((shape.heads, n_p), dtype=torch.float32, device=dev) if want_scores else None
+    _check(_lib.bsga_probe_select(ctypes.byref(shape.c()), _ptr(q), _ptr(k), int(topk),
+                                  _ptr(scores), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                  _ws_ptr(ws), _ws_len(ws), _stream(dev)), "bsga_probe_select")
+    return (row_ptr, col_idx, scores) if want_scores else (row_ptr, col_idx)
 
 
 def _outputs(shape: LayerShape, q: torch.Tensor, o, lse):

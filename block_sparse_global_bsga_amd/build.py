@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsga.so")
-SOURCES = ["bsga_api.cpp", "budget.cpp", "predict.hip", "select.hip", "attention.hip"]
+SOURCES = ["bsga_api.cpp", "budget.cpp", "predict.hip", "select.hip", "probe.hip",
+           "attention.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

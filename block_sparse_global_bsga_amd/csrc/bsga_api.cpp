@@ -76,6 +76,7 @@ size_t ws_predict(const Dims& d) { return 2 * up((size_t)d.H * d.B * kHeadDim * 
 size_t ws_select(const Dims& d) { return up(select_workspace(d)); }
 size_t ws_pack(const Dims& d) { return up(pack_bytes(d)); }
 size_t ws_special(const Dims& d) { return up(special_workspace(d)); }
+size_t ws_probe(const Dims& d) { return up(probe_workspace(d)); }
 
 size_t ws_for(const Dims& d, int op) {
   switch (op) {
@@ -85,6 +86,7 @@ size_t ws_for(const Dims& d, int op) {
     case BSGA_OP_SPECIAL_DENSE: return ws_pack(d) + ws_special(d);
     case BSGA_OP_DENSE_ATTN: return ws_pack(d);
     case BSGA_OP_SPECIAL_DENSE_PACKED: return ws_special(d);
+    case BSGA_OP_PROBE_SELECT: return ws_probe(d);
     case BSGA_OP_LAYER: {
       size_t m = ws_predict(d);
       if (ws_select(d) > m) m = ws_select(d);
@@ -187,7 +189,7 @@ int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries) {
 
 int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes) {
   BSGA_TRY(check_shape(shape));
-  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_SPECIAL_DENSE_PACKED)
+  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_PROBE_SELECT)
     return BSGA_ERR_INVALID_ARG;
   *bytes = ws_for(make_dims(*shape), op);
   return BSGA_OK;
@@ -223,6 +225,21 @@ int bsga_select(const bsga_shape* shape, const float* probs, const double* rho_p
   BSGA_TRY(fill_select_params(d, rho_per_head, rho, tau, &sp));
   BSGA_TRY(check_ws(d, BSGA_OP_SELECT, ws, ws_bytes));
   return hip_status(launch_select(d, probs, sp, row_ptr, col_idx, ws, (hipStream_t)stream));
+}
+
+int bsga_probe_select(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, int32_t topk,
+                      float* scores, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                      void* ws, size_t ws_bytes, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_select_shape(d));
+  BSGA_TRY(check_qk(q, k));
+  if (topk < 0) return BSGA_ERR_INVALID_ARG;
+  if (scores && ((uintptr_t)scores % 4)) return BSGA_ERR_MISALIGNED;
+  BSGA_TRY(check_csr(d, row_ptr, col_idx, col_capacity));
+  BSGA_TRY(check_ws(d, BSGA_OP_PROBE_SELECT, ws, ws_bytes));
+  return hip_status(launch_probe_select(d, q, k, topk, scores, row_ptr, col_idx, ws,
+                                        (hipStream_t)stream));
 }
 
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -118,6 +118,11 @@ hipError_t launch_select(const Dims& d, const float* probs,
                          const SelectParams& sp, int32_t* row_ptr,
                          int32_t* col_idx, void* ws, hipStream_t st);
 
+size_t probe_workspace(const Dims& d);
+hipError_t launch_probe_select(const Dims& d, const uint16_t* q, const uint16_t* k, int topk,
+                               float* scores, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                               hipStream_t st);
+
 size_t pack_bytes(const Dims& d);  // packed K and V^T
 hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v,
                        uint16_t* kp, uint16_t* vt, hipStream_t st);

@@ -68,7 +68,8 @@ typedef enum bsga_op {
   BSGA_OP_SPECIAL_DENSE = 3,
   BSGA_OP_DENSE_ATTN = 4,
   BSGA_OP_LAYER = 5,
-  BSGA_OP_SPECIAL_DENSE_PACKED = 6
+  BSGA_OP_SPECIAL_DENSE_PACKED = 6,
+  BSGA_OP_PROBE_SELECT = 7
 } bsga_op;
 
 /* Shape of one global-attention layer.  head_dim must be 64; block (b) must
@@ -154,6 +155,30 @@ int bsga_select(const bsga_shape* shape, const float* probs,
                 const double* rho_per_head, double rho, double tau,
                 int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Query-probe Top-K block selection ("SAF3R: Dynamic Sparse Attention for
+ * Feed-Forward 3D Reconstruction Transformers", cited as [SAF3R], section 4:
+ * the query-probe Top-K kernel for heads whose queries share a few dominant
+ * keys, with its O(N) online estimate).  Per head h:
+ *   qbar = (1/N) sum over all N tokens of Q[h][t]           (the probe),
+ *   r_p  = qbar . K[h][patch p] / sqrt(64)   for every patch key p,
+ * which equals the mean over all queries of their score with key p.  The
+ * `topk` patch keys with the largest r_p (ties: lower patch index first) are
+ * taken, and every query block of the head keeps the patch blocks holding at
+ * least one of them, in ascending order (same CSR layout as bsga_select, all
+ * rows of a head equal).  Special keys are not ranked: they stay dense in the
+ * attention calls.
+ *   q, k: [H][N][64] bf16.  topk >= 0 (0 keeps no block; >= N_p keeps all).
+ *   scores: optional [H][N_p] float32 output of r (patch order), or NULL.
+ *   row_ptr [H*B+1], col_idx (capacity >= H*B*B) as for bsga_select.
+ *   workspace: bsga_workspace_bytes(BSGA_OP_PROBE_SELECT).  Requires
+ *   B <= BSGA_MAX_BLOCKS.  Float32 mean and dot products; the ranking uses the
+ *   float32 r exactly as written to `scores`. */
+int bsga_probe_select(const bsga_shape* shape, const uint16_t* q,
+                      const uint16_t* k, int32_t topk, float* scores,
+                      int32_t* row_ptr, int32_t* col_idx,
+                      int64_t col_capacity, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Block-sparse attention of the patch queries over their kept patch blocks
  * ([BSGA] equation SparseAttn, masked entries excluded from the softmax):

@@ -47,7 +47,15 @@ design document):
   tokens of their kept blocks, all in one softmax;
 * head-wise budgets ([HeSS], iterative capping, no formula given): keep
   fractions 1 - rho_h proportional to positive per-head weights, clipped to
-  [1 - rho_max, 1 - rho_min], with their mean fixed at 1 - mean_rho.
+  [1 - rho_max, 1 - rho_min], with their mean fixed at 1 - mean_rho;
+* query probe ([SAF3R] section 4): the probe is the mean query of all N tokens
+  of the head; only patch keys are ranked (special keys stay dense); ties go to
+  the lower patch index; the top-k keys are mapped to the patch blocks that
+  hold them, and every query block of the head keeps those blocks.
+
+[SAF3R] "SAF3R: Dynamic Sparse Attention for Feed-Forward 3D Reconstruction
+Transformers" (news page), section 4 (query-probe Top-K kernel and its online
+estimate through the mean query).
 """
 from __future__ import annotations
 
@@ -303,3 +311,26 @@ def redistribute_budget(weights: Sequence[float], mean_rho: float, rho_min: floa
             lam = a if fb == fa else a + (target - fa) * (b - a) / (fb - fa)
             break
     return [float(1 - min(max(lam * x, lo), hi)) for x in w]
+
+
+# ----------------------------------------------------------------------------
+# query-probe Top-K selection  ([SAF3R] section 4: query-probe Top-K kernel)
+# ----------------------------------------------------------------------------
+def probe_scores(q: np.ndarray, k: np.ndarray, frames: int, patches_per_frame: int,
+                 special_per_frame: int) -> np.ndarray:
+    """Score of every patch key against the mean query of all N tokens,
+    qbar . k_p / sqrt(d_h), in patch order."""
+    _, patch = token_roles(frames, patches_per_frame, special_per_frame)
+    qbar = q.mean(axis=0)
+    return (k[patch] @ qbar) / math.sqrt(q.shape[1])
+
+
+def probe_blocks(scores: np.ndarray, block: int, topk: int) -> np.ndarray:
+    """Patch blocks (ascending) holding at least one of the topk best patch
+    keys, keys ranked by score descending, then lower patch index."""
+    n = scores.shape[0]
+    kk = max(0, min(int(topk), n))
+    if kk == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(n), -scores))
+    return np.unique(order[:kk] // block)

@@ -438,4 +438,36 @@ def pin_budget_invariants(O):
     assert np.allclose(1 - np.array(rho), 4 * 0.25 * w / w.sum(), atol=1e-15)
 
 
+def pin_probe_golden(O):
+    """[SAF3R] section 4: hand-worked ranking, tie and block mapping, and a
+    hand-worked probe (mean query over all tokens, specials included)."""
+    g = _golden("probe_worked.json")
+    sc = np.array(g["scores"], dtype=np.float64)
+    for c in g["cases"]:
+        got = O.probe_blocks(sc, g["block"], c["topk"]).tolist()
+        assert got == c["blocks"], (c, got)
+    pr = g["probe"]
+    r = O.probe_scores(np.array(pr["q"], dtype=np.float64), np.array(pr["k"], dtype=np.float64),
+                       pr["frames"], pr["patches_per_frame"], pr["special_per_frame"])
+    assert np.allclose(r, pr["scores"], atol=1e-15), r
+
+
+def pin_probe_identity(O):
+    """The probe score of a key equals the mean over all queries of the full
+    score matrix column (the page's linearity argument, computed the long way
+    round), and a planted key aligned with the mean query ranks first."""
+    rng = np.random.default_rng(23)
+    F, P, S, D = 3, 20, 5, 16
+    N = F * (P + S)
+    q = rng.standard_normal((N, D)) + 0.7
+    k = rng.standard_normal((N, D))
+    _, patch = O.token_roles(F, P, S)
+    full = (q @ k.T) / math.sqrt(D)
+    r = O.probe_scores(q, k, F, P, S)
+    assert np.allclose(r, full.mean(axis=0)[patch], atol=1e-12)
+    k[patch[37]] = 5.0 * q.mean(axis=0)
+    r = O.probe_scores(q, k, F, P, S)
+    assert O.probe_blocks(r, 8, 1).tolist() == [37 // 8]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -64,6 +64,26 @@ def test_capacity_and_workspace_sizes():
     sizes = {op: bsga.workspace_bytes(shape, op) for op in range(6)}
     assert sizes[bsga.OP_LAYER] >= max(sizes.values()) - 1
     assert sizes[bsga.OP_SPARSE_ATTN] >= 2 * 16 * (43904 + 256) * 64 * 2
+    # probe selection: partial sums, mean query, scores, block lists, counts
+    assert bsga.workspace_bytes(shape, bsga.OP_PROBE_SELECT) >= 16 * 43808 * 4
+    out = ctypes.c_size_t()
+    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PROBE_SELECT + 1,
+                                    ctypes.byref(out)) == bsga.ERR_INVALID_ARG
+
+
+def test_probe_select_validation():
+    """Argument checks of bsga_probe_select run before any launch (no GPU)."""
+    shape = S(2, 16, 5, 2, 64)
+    c = shape.c()
+    buf = (ctypes.c_uint8 * 4096)()
+    p16 = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 256
+    cap = bsga.csr_capacity(shape)
+    ok_args = [ctypes.byref(c), p16, p16, 3, None, p16, p16, cap, p16, 1 << 40, None]
+    for i, bad in [(1, None), (2, p16 + 2), (3, -1), (4, p16 + 2), (5, None), (7, cap - 1),
+                   (8, None)]:
+        args = list(ok_args)
+        args[i] = bad
+        assert lib.bsga_probe_select(*args) != bsga.OK, i
 
 
 def _status(fn, *args):

@@ -216,12 +216,34 @@ def _budget_inverse(O):
     O.redistribute_budget = lambda w, *a: real([1.0 / x for x in w], *a)
 
 
+def _probe_patch_queries_only(O):
+    def f(q, k, frames, P, S):
+        _, patch = O.token_roles(frames, P, S)
+        return (k[patch] @ q[patch].mean(axis=0)) / math.sqrt(q.shape[1])
+    O.probe_scores = f
+
+
+def _probe_ascending(O):
+    real = O.probe_blocks
+    O.probe_blocks = lambda scores, block, topk: real(-scores, block, topk)
+
+
+def _probe_tie_high_index(O):
+    def f(scores, block, topk):
+        n = scores.shape[0]
+        kk = max(0, min(int(topk), n))
+        order = np.lexsort((-np.arange(n), -scores))
+        return np.unique(order[:kk] // block) if kk else np.zeros(0, dtype=np.int64)
+    O.probe_blocks = f
+
+
 MUTANTS = [_no_scale, _transposed_scores, _softmax_wrong_axis, _ascending_rank,
            _tie_high_index, _strict_coverage, _coverage_off_by_one,
            _min_not_max, _ceil_keep, _binary_float_keep, _pool_divides_by_b,
            _specials_last, _attn_no_scale, _lse_no_max, _masked_as_zero_logit,
            _no_special_keys, _special_queries_sparse, _entries_ignore_partial,
-           _budget_one_sided, _budget_unclipped, _budget_inverse]
+           _budget_one_sided, _budget_unclipped, _budget_inverse,
+           _probe_patch_queries_only, _probe_ascending, _probe_tie_high_index]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
