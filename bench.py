@@ -216,6 +216,21 @@ def main():
                    for j, name in enumerate(stages)}
         return total, per
 
+    def timed_marks(fn, steps, warmup, marks):
+        """Average ms per step and per interval between `marks` events."""
+        for _ in range(warmup):
+            fn(None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            fn(evs[i])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(marks - 1)]
+        return start.elapsed_time(stop) / steps, parts
+
     print(f"# warmup {args.warmup} + {args.steps} timed layer steps, {cfg.name}", file=sys.stderr,
           flush=True)
     ms, stage_ms = timed(lambda ev: step(cfg.rho, cfg.tau, ev), args.steps, args.warmup, True)
@@ -224,6 +239,7 @@ def main():
     ci = col_idx[:int(rp[-1])].cpu().numpy()
     pp, sp = computed_entries(rp, ci, cfg.n_patch, cfg.block, cfg.heads, cfg.n_special)
     n = cfg.tokens
+    tok_bytes = cfg.heads * HEAD_DIM * 2  # one token row of every head, bf16
     density = (pp + sp) / (cfg.heads * n * n)
     layer_tflops = 4 * HEAD_DIM * (pp + sp) / (ms * 1e-3) / 1e12
     # the patch-row kernel computes the kept patch-patch entries plus N_p x N_s
@@ -250,7 +266,53 @@ def main():
                                     cfg.block, cfg.heads, cfg.n_special)
         print(f"# dense {dense_ms:.3f} ms; bsga_layer call {layer_call_ms:.3f} ms; "
               f"tau=0: {ms0:.3f} ms", file=sys.stderr, flush=True)
+        # query-probe Top-K lists (1 % of the patch keys) and the attention over them
+        topk = max(1, cfg.n_patch // 100)
+        ws_probe = bsga.workspace(shape, bsga.OP_PROBE_SELECT, dev)
+
+        def probe_step(ev):
+            mark = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+            mark(0)
+            bsga.probe_select(shape, q, k, topk, row_ptr=row_ptr, col_idx=col_idx, ws=ws_probe)
+            mark(1)
+            bsga.pack_kv(shape, k, v, kv=kv)
+            bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
+            bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
+            mark(2)
+
+        probe_ms, probe_parts = timed_marks(probe_step, max(3, args.steps // 2), 2, 3)
+        rpp = row_ptr.cpu().numpy()
+        ppp, spp = computed_entries(rpp, col_idx[:int(rpp[-1])].cpu().numpy(), cfg.n_patch,
+                                    cfg.block, cfg.heads, cfg.n_special)
+        probe_bytes = tok_bytes * (n + cfg.n_patch) + cfg.heads * cfg.n_patch * 4
+        # sparse-vs-dense NMSE per head type, with and without the dense special path
+        o_dense, _ = bsga.dense_attn(shape, q, k, v)
+        ws_nmse = bsga.workspace(shape, bsga.OP_NMSE, dev)
+        nm_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        layer_std = bsga.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head, bufs=bufs)
+        nm_ev[0].record(stream)
+        nm_std = bsga.nmse(shape, o_dense, layer_std.o, ws=ws_nmse)
+        nm_ev[1].record(stream)
+        pooled = bsga.pooled_specials_shape(shape)
+        layer_pool = bsga.layer(pooled, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+        nm_pool = bsga.nmse(shape, o_dense, layer_pool.o, ws=ws_nmse)
+        torch.cuda.synchronize()
+        nmse_ms = nm_ev[0].elapsed_time(nm_ev[1])
+        by_type = {}
+        for name, vals in (("standard", nm_std), ("pooled_specials", nm_pool)):
+            vals = vals.cpu().numpy()
+            by_type[name] = {t: float(np.mean([vals[h] for h in range(cfg.heads)
+                                              if x.head_types[h] == t]))
+                             for t in sorted(set(x.head_types))}
+        del layer_pool
         extras = {
+            "probe_topk": {"topk": topk, "select_ms": round(probe_parts[0], 4),
+                           "select_GB/s": round(probe_bytes / (probe_parts[0] * 1e-3) / 1e9, 1),
+                           "attention_ms": round(probe_parts[1], 4),
+                           "density": round((ppp + spp) / (cfg.heads * n * n), 4)},
+            "nmse_vs_dense_by_head_type": by_type,
+            "nmse_kernel": {"ms": round(nmse_ms, 4),
+                            "GB/s": round(2 * tok_bytes * n / (nmse_ms * 1e-3) / 1e9, 1)},
             "dense_ms": round(dense_ms, 4),
             "speedup_vs_dense": round(dense_ms / ms, 3),
             "bsga_layer_call_ms": round(layer_call_ms, 4),
@@ -265,7 +327,6 @@ def main():
 
     # algorithmic HBM bytes of the bandwidth-bound stages (bf16 = 2 bytes)
     nnz = int(rp[-1])
-    tok_bytes = cfg.heads * HEAD_DIM * 2
     stage_bytes = {
         "predict_mask": 2 * cfg.n_patch * tok_bytes + cfg.heads * B * B * 4,
         "select": cfg.heads * B * B * 4 + (cfg.heads * B + 1 + nnz) * 4,

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 (OP_PREDICT_MASK, OP_SELECT, OP_SPARSE_ATTN, OP_SPECIAL_DENSE, OP_DENSE_ATTN, OP_LAYER,
- OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT) = range(8)
+ OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT, OP_NMSE) = range(9)
 MAX_HEADS = 256
 MAX_BLOCKS = 4096
 
@@ -37,7 +37,7 @@ EXPORTS = [
     "bsga_select", "bsga_sparse_attn", "bsga_special_dense", "bsga_dense_attn",
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
-    "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select",
+    "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select", "bsga_nmse",
 ]
 
 
@@ -63,6 +63,7 @@ _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, 
                              ctypes.c_int64, _p, ctypes.c_size_t, _p]
 _lib.bsga_probe_select.argtypes = [_sp, _p, _p, ctypes.c_int32, _p, _p, _p, ctypes.c_int64, _p,
                                    ctypes.c_size_t, _p]
+_lib.bsga_nmse.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_sparse_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_special_dense.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_dense_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -258,6 +259,25 @@ def probe_select(shape: LayerShape, q: torch.Tensor, k: torch.Tensor, topk: int,
                                   _ptr(scores), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                                   _ws_ptr(ws), _ws_len(ws), _stream(dev)), "bsga_probe_select")
     return (row_ptr, col_idx, scores) if want_scores else (row_ptr, col_idx)
+
+
+def nmse(shape: LayerShape, o_ref: torch.Tensor, o: torch.Tensor, *,
+         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head ||o_ref - o||^2 / ||o_ref||^2 (float64 [H] on the device)."""
+    o_ref, o = _bf16(o_ref, "o_ref", shape), _bf16(o, "o", shape)
+    dev = o.device
+    out = torch.empty(shape.heads, dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = workspace(shape, OP_NMSE, dev)
+    _check(_lib.bsga_nmse(ctypes.byref(shape.c()), _ptr(o_ref), _ptr(o), _ptr(out), _ws_ptr(ws),
+                          _ws_len(ws), _stream(dev)), "bsga_nmse")
+    return out
+
+
+def pooled_specials_shape(shape: LayerShape) -> LayerShape:
+    """The ablation without a dense special path: the whole token sequence as
+    one run of blocks (special tokens pooled with the patches)."""
+    return LayerShape(1, shape.tokens, 0, shape.heads, shape.block)
 
 
 def _outputs(shape: LayerShape, q: torch.Tensor, o, lse):

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsga.so")
 SOURCES = ["bsga_api.cpp", "budget.cpp", "predict.hip", "select.hip", "probe.hip",
-           "attention.hip"]
+           "metrics.hip", "attention.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

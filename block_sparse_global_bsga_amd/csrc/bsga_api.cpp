@@ -77,6 +77,7 @@ size_t ws_select(const Dims& d) { return up(select_workspace(d)); }
 size_t ws_pack(const Dims& d) { return up(pack_bytes(d)); }
 size_t ws_special(const Dims& d) { return up(special_workspace(d)); }
 size_t ws_probe(const Dims& d) { return up(probe_workspace(d)); }
+size_t ws_nmse(const Dims& d) { return up(nmse_workspace(d)); }
 
 size_t ws_for(const Dims& d, int op) {
   switch (op) {
@@ -87,6 +88,7 @@ size_t ws_for(const Dims& d, int op) {
     case BSGA_OP_DENSE_ATTN: return ws_pack(d);
     case BSGA_OP_SPECIAL_DENSE_PACKED: return ws_special(d);
     case BSGA_OP_PROBE_SELECT: return ws_probe(d);
+    case BSGA_OP_NMSE: return ws_nmse(d);
     case BSGA_OP_LAYER: {
       size_t m = ws_predict(d);
       if (ws_select(d) > m) m = ws_select(d);
@@ -189,7 +191,7 @@ int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries) {
 
 int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes) {
   BSGA_TRY(check_shape(shape));
-  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_PROBE_SELECT)
+  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_NMSE)
     return BSGA_ERR_INVALID_ARG;
   *bytes = ws_for(make_dims(*shape), op);
   return BSGA_OK;
@@ -240,6 +242,17 @@ int bsga_probe_select(const bsga_shape* shape, const uint16_t* q, const uint16_t
   BSGA_TRY(check_ws(d, BSGA_OP_PROBE_SELECT, ws, ws_bytes));
   return hip_status(launch_probe_select(d, q, k, topk, scores, row_ptr, col_idx, ws,
                                         (hipStream_t)stream));
+}
+
+int bsga_nmse(const bsga_shape* shape, const uint16_t* o_ref, const uint16_t* o, double* nmse,
+              void* ws, size_t ws_bytes, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_ptr(o_ref, 16));
+  BSGA_TRY(check_ptr(o, 16));
+  BSGA_TRY(check_ptr(nmse, 8));
+  BSGA_TRY(check_ws(d, BSGA_OP_NMSE, ws, ws_bytes));
+  return hip_status(launch_nmse(d, o_ref, o, nmse, ws, (hipStream_t)stream));
 }
 
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -69,7 +69,8 @@ typedef enum bsga_op {
   BSGA_OP_DENSE_ATTN = 4,
   BSGA_OP_LAYER = 5,
   BSGA_OP_SPECIAL_DENSE_PACKED = 6,
-  BSGA_OP_PROBE_SELECT = 7
+  BSGA_OP_PROBE_SELECT = 7,
+  BSGA_OP_NMSE = 8
 } bsga_op;
 
 /* Shape of one global-attention layer.  head_dim must be 64; block (b) must
@@ -210,6 +211,22 @@ int bsga_dense_attn(const bsga_shape* shape, const uint16_t* q,
                     const uint16_t* k, const uint16_t* v, uint16_t* o,
                     float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Normalised mean squared error per head ([SAF3R] section 4, offline head
+ * profiling):  nmse[h] = ||o_ref[h] - o[h]||^2 / ||o_ref[h]||^2  over all N
+ * rows and 64 dims of the head (0 when both are zero, +inf when only the
+ * reference is).  o_ref, o: [H][N][64] bf16 (e.g. the dense and a sparse
+ * output).  nmse: DEVICE array of H doubles (output).  Float32 sums per
+ * chunk of 1024 rows, float64 across chunks, in a fixed order
+ * (deterministic).  Workspace: bsga_workspace_bytes(BSGA_OP_NMSE).
+ *
+ * Ablation without the dense special path ([BSGA] ablation of the special-
+ * token design): pass every call the shape {frames = 1, patches_per_frame =
+ * N, special_per_frame = 0}; blocks then run over the whole token sequence,
+ * so the special tokens are pooled and selected together with the patches. */
+int bsga_nmse(const bsga_shape* shape, const uint16_t* o_ref, const uint16_t* o,
+              double* nmse, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 /* Packed K/V: the layout the attention kernels stream.  Keys are listed in
  * "packed order" — the N_p patch tokens in patch order, zero rows up to the

@@ -334,3 +334,15 @@ def probe_blocks(scores: np.ndarray, block: int, topk: int) -> np.ndarray:
         return np.zeros(0, dtype=np.int64)
     order = np.lexsort((np.arange(n), -scores))
     return np.unique(order[:kk] // block)
+
+
+# ----------------------------------------------------------------------------
+# output error  ([SAF3R] section 4, offline head profiling)
+# ----------------------------------------------------------------------------
+def nmse(o_full: np.ndarray, o_sparse: np.ndarray) -> float:
+    """||O_full - O_sparse||^2 / ||O_full||^2 over all entries of one head."""
+    num = float(np.sum((o_full - o_sparse) ** 2))
+    den = float(np.sum(o_full ** 2))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den

@@ -470,4 +470,17 @@ def pin_probe_identity(O):
     assert O.probe_blocks(r, 8, 1).tolist() == [37 // 8]
 
 
+def pin_nmse_closed_forms(O):
+    """||A - B||^2 / ||A||^2: zero for equal outputs, one against zero,
+    (1 - c)^2 for B = c A, and a hand-worked pair."""
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((7, 4))
+    assert O.nmse(a, a) == 0.0
+    assert abs(O.nmse(a, np.zeros_like(a)) - 1.0) < 1e-15
+    assert abs(O.nmse(a, 0.25 * a) - 0.5625) < 1e-14
+    x = np.array([[3.0, 4.0]])
+    assert abs(O.nmse(x, np.array([[3.0, 2.0]])) - 4.0 / 25.0) < 1e-15
+    assert O.nmse(np.zeros((2, 2)), np.zeros((2, 2))) == 0.0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

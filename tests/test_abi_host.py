@@ -66,8 +66,10 @@ def test_capacity_and_workspace_sizes():
     assert sizes[bsga.OP_SPARSE_ATTN] >= 2 * 16 * (43904 + 256) * 64 * 2
     # probe selection: partial sums, mean query, scores, block lists, counts
     assert bsga.workspace_bytes(shape, bsga.OP_PROBE_SELECT) >= 16 * 43808 * 4
+    # per-head NMSE: one float64 pair per head and chunk of 1024 rows
+    assert bsga.workspace_bytes(shape, bsga.OP_NMSE) >= 16 * 43 * 16
     out = ctypes.c_size_t()
-    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PROBE_SELECT + 1,
+    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_NMSE + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 
 

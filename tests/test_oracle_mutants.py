@@ -237,13 +237,22 @@ def _probe_tie_high_index(O):
     O.probe_blocks = f
 
 
+def _nmse_normalised_by_sparse(O):
+    O.nmse = lambda a, b: float(np.sum((a - b) ** 2) / max(np.sum(b ** 2), 1e-300))
+
+
+def _nmse_no_square(O):
+    O.nmse = lambda a, b: float(np.sum(np.abs(a - b)) / max(np.sum(np.abs(a)), 1e-300))
+
+
 MUTANTS = [_no_scale, _transposed_scores, _softmax_wrong_axis, _ascending_rank,
            _tie_high_index, _strict_coverage, _coverage_off_by_one,
            _min_not_max, _ceil_keep, _binary_float_keep, _pool_divides_by_b,
            _specials_last, _attn_no_scale, _lse_no_max, _masked_as_zero_logit,
            _no_special_keys, _special_queries_sparse, _entries_ignore_partial,
            _budget_one_sided, _budget_unclipped, _budget_inverse,
-           _probe_patch_queries_only, _probe_ascending, _probe_tie_high_index]
+           _probe_patch_queries_only, _probe_ascending, _probe_tie_high_index,
+           _nmse_normalised_by_sparse, _nmse_no_square]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
