@@ -346,3 +346,52 @@ def nmse(o_full: np.ndarray, o_sparse: np.ndarray) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else math.inf
     return num / den
+
+
+# ----------------------------------------------------------------------------
+# backward of the layer's attention for a fixed mask  ([BSGA] outlook: sparse
+# attention inside training; the block selection itself is not differentiated)
+# ----------------------------------------------------------------------------
+def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_o: np.ndarray,
+                            frames: int, patches_per_frame: int, special_per_frame: int,
+                            block: int, kept: Optional[List[np.ndarray]]):
+    """Gradients (dQ, dK, dV) of L = sum(O * dO) for one head, where O is the
+    layer's output (patch queries over their kept patch blocks and every
+    special key, special queries over every key; kept = None: dense).
+
+    Per query, with its allowed keys t, logits l_t = q . k_t / sqrt(d),
+    P_t = softmax(l)_t and O = sum_t P_t v_t:
+      dV_t += P_t dO,  dP_t = dO . v_t,  D = dO . O,  dS_t = P_t (dP_t - D),
+      dQ = sum_t dS_t k_t / sqrt(d),  dK_t += dS_t q / sqrt(d).
+    Computed one query block (and the special queries) at a time."""
+    spec, patch = token_roles(frames, patches_per_frame, special_per_frame)
+    n = patch.shape[0]
+    B = num_blocks(n, block)
+    scale = 1.0 / math.sqrt(q.shape[1])
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    all_tok = np.arange(q.shape[0])
+    groups = []
+    for i in range(B):
+        qt = patch[block_members(n, block, i)]
+        if kept is None:
+            keys = all_tok
+        else:
+            keys = np.concatenate([patch_block_tokens(patch, block, kept[i]), spec])
+        groups.append((qt, keys))
+    if spec.shape[0]:
+        groups.append((spec, all_tok))
+    for qt, keys in groups:
+        if keys.shape[0] == 0:
+            continue
+        logits = (q[qt] @ k[keys].T) * scale
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        o = p @ v[keys]
+        dp = d_o[qt] @ v[keys].T
+        dd = np.sum(d_o[qt] * o, axis=1, keepdims=True)
+        ds = p * (dp - dd)
+        dq[qt] += (ds @ k[keys]) * scale
+        np.add.at(dk, keys, (ds.T @ q[qt]) * scale)
+        np.add.at(dv, keys, p.T @ d_o[qt])
+    return dq, dk, dv

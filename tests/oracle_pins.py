@@ -483,4 +483,76 @@ def pin_nmse_closed_forms(O):
     assert O.nmse(np.zeros((2, 2)), np.zeros((2, 2))) == 0.0
 
 
+def _tiny_backward_case(seed=0):
+    rng = np.random.default_rng(seed)
+    F, P, S, b, D = 2, 6, 1, 2, 4
+    N = F * (P + S)
+    q, k, v, do = (rng.standard_normal((N, D)) for _ in range(4))
+    B = (F * P + b - 1) // b
+    kept = [np.array(sorted(rng.choice(B, size=2, replace=False))) for _ in range(B)]
+    return (F, P, S, b), q, k, v, do, kept
+
+
+def pin_backward_finite_differences(O):
+    """Gradients of L = sum(O * dO) against central differences of the
+    oracle's own forward (layer_head), on a tiny masked layer."""
+    (F, P, S, b), q, k, v, do, kept = _tiny_backward_case()
+    dq, dk, dv = O.attention_backward_head(q, k, v, do, F, P, S, b, kept)
+
+    def loss(q_, k_, v_):
+        out = O.layer_head(q_, k_, v_, F, P, S, b, kept)
+        return sum(float(np.dot(out[t][0], do[t])) for t in out)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in list(np.ndindex(x.shape))[::3]:
+            args = {"q_": q, "k_": k, "v_": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name + "_"] = xp
+            lp = loss(**args)
+            args[name + "_"] = xm
+            lm = loss(**args)
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 1e-7, (name, idx)
+
+
+def pin_backward_autograd(O):
+    """The same gradients from torch autograd of a plain masked softmax
+    attention in float64 (mask written out token by token)."""
+    import torch
+    (F, P, S, b), q, k, v, do, kept = _tiny_backward_case(1)
+    spec, patch = O.token_roles(F, P, S)
+    N = q.shape[0]
+    allowed = np.zeros((N, N), dtype=bool)
+    allowed[spec, :] = True
+    allowed[:, spec] = True
+    for pi, qt in enumerate(patch):
+        for pj, kt in enumerate(patch):
+            if (pj // b) in set(kept[pi // b].tolist()):
+                allowed[qt, kt] = True
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    logits = (tq @ tk.T) / math.sqrt(q.shape[1])
+    logits = logits.masked_fill(~torch.tensor(allowed), float("-inf"))
+    out = torch.softmax(logits, dim=1) @ tv
+    (out * torch.tensor(do)).sum().backward()
+    dq, dk, dv = O.attention_backward_head(q, k, v, do, F, P, S, b, kept)
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.allclose(g, t.grad.numpy(), atol=1e-12)
+
+
+def pin_backward_closed_forms(O):
+    """A query with a single allowed key has zero logit gradients (dQ = dK =
+    0) and passes dO straight to that key's dV; dense gradients of dV sum to
+    the column sums of dO (softmax rows sum to 1)."""
+    rng = np.random.default_rng(4)
+    q, k, v, do = (rng.standard_normal((3, 4)) for _ in range(4))
+    # one frame, no specials, blocks of 1 token, each query keeps only its own block
+    dq, dk, dv = O.attention_backward_head(q, k, v, do, 1, 3, 0, 1,
+                                           [np.array([0]), np.array([1]), np.array([2])])
+    assert np.allclose(dq, 0.0, atol=1e-15) and np.allclose(dk, 0.0, atol=1e-15)
+    assert np.allclose(dv, do, atol=1e-15)
+    dq, dk, dv = O.attention_backward_head(q, k, v, do, 1, 3, 0, 1, None)
+    assert np.allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -245,6 +245,48 @@ def _nmse_no_square(O):
     O.nmse = lambda a, b: float(np.sum(np.abs(a - b)) / max(np.sum(np.abs(a)), 1e-300))
 
 
+def _backward_without_d(O):
+    # treats dS as P * dP, dropping the D = dO . O term of the softmax Jacobian
+    def f(q, k, v, d_o, frames, P, S, block, kept):
+        spec, patch = O.token_roles(frames, P, S)
+        n = patch.shape[0]
+        scale = 1.0 / math.sqrt(q.shape[1])
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        groups = []
+        for i in range(O.num_blocks(n, block)):
+            qt = patch[O.block_members(n, block, i)]
+            keys = (np.arange(q.shape[0]) if kept is None else
+                    np.concatenate([O.patch_block_tokens(patch, block, kept[i]), spec]))
+            groups.append((qt, keys))
+        if spec.shape[0]:
+            groups.append((spec, np.arange(q.shape[0])))
+        for qt, keys in groups:
+            logits = (q[qt] @ k[keys].T) * scale
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            ds = p * (d_o[qt] @ v[keys].T)
+            dq[qt] += (ds @ k[keys]) * scale
+            np.add.at(dk, keys, (ds.T @ q[qt]) * scale)
+            np.add.at(dv, keys, p.T @ d_o[qt])
+        return dq, dk, dv
+    O.attention_backward_head = f
+
+
+def _backward_dense_mask(O):
+    real = O.attention_backward_head
+    O.attention_backward_head = lambda q, k, v, d_o, F, P, S, b, kept: real(q, k, v, d_o, F, P, S,
+                                                                             b, None)
+
+
+def _backward_unscaled_dk(O):
+    real = O.attention_backward_head
+
+    def f(*a):
+        dq, dk, dv = real(*a)
+        return dq, dk * math.sqrt(a[0].shape[1]), dv
+    O.attention_backward_head = f
+
+
 MUTANTS = [_no_scale, _transposed_scores, _softmax_wrong_axis, _ascending_rank,
            _tie_high_index, _strict_coverage, _coverage_off_by_one,
            _min_not_max, _ceil_keep, _binary_float_keep, _pool_divides_by_b,
@@ -252,7 +294,8 @@ MUTANTS = [_no_scale, _transposed_scores, _softmax_wrong_axis, _ascending_rank,
            _no_special_keys, _special_queries_sparse, _entries_ignore_partial,
            _budget_one_sided, _budget_unclipped, _budget_inverse,
            _probe_patch_queries_only, _probe_ascending, _probe_tie_high_index,
-           _nmse_normalised_by_sparse, _nmse_no_square]
+           _nmse_normalised_by_sparse, _nmse_no_square,
+           _backward_without_d, _backward_dense_mask, _backward_unscaled_dk]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
