@@ -392,6 +392,7 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_o: np
         dd = np.sum(d_o[qt] * o, axis=1, keepdims=True)
         ds = p * (dp - dd)
         dq[qt] += (ds @ k[keys]) * scale
-        np.add.at(dk, keys, (ds.T @ q[qt]) * scale)
-        np.add.at(dv, keys, p.T @ d_o[qt])
+        # the keys of one query group are distinct, so a plain indexed add is exact
+        dk[keys] += (ds.T @ q[qt]) * scale
+        dv[keys] += p.T @ d_o[qt]
     return dq, dk, dv
