@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 (OP_PREDICT_MASK, OP_SELECT, OP_SPARSE_ATTN, OP_SPECIAL_DENSE, OP_DENSE_ATTN, OP_LAYER,
- OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT, OP_NMSE) = range(9)
+ OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT, OP_NMSE, OP_BACKWARD) = range(10)
 MAX_HEADS = 256
 MAX_BLOCKS = 4096
 
@@ -38,6 +38,7 @@ EXPORTS = [
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
     "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select", "bsga_nmse",
+    "bsga_attn_backward",
 ]
 
 
@@ -64,6 +65,8 @@ _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, 
 _lib.bsga_probe_select.argtypes = [_sp, _p, _p, ctypes.c_int32, _p, _p, _p, ctypes.c_int64, _p,
                                    ctypes.c_size_t, _p]
 _lib.bsga_nmse.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.bsga_attn_backward.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                    ctypes.c_size_t, _p]
 _lib.bsga_sparse_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_special_dense.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_dense_attn.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -272,6 +275,27 @@ def nmse(shape: LayerShape, o_ref: torch.Tensor, o: torch.Tensor, *,
     _check(_lib.bsga_nmse(ctypes.byref(shape.c()), _ptr(o_ref), _ptr(o), _ptr(out), _ws_ptr(ws),
                           _ws_len(ws), _stream(dev)), "bsga_nmse")
     return out
+
+
+def attn_backward(shape: LayerShape, q, k, v, o, lse, d_o, row_ptr, col_idx, *,
+                  dq=None, dk=None, dv=None, ws: Optional[torch.Tensor] = None):
+    """Gradients (dQ, dK, dV) [H][N][64] float32 of the layer's attention for
+    the mask (row_ptr, col_idx) that produced o and lse."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _bf16(t, n, shape)
+    dev = q.device
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty((shape.heads, shape.tokens, 64), dtype=torch.float32, device=dev)
+        grads.append(g)
+    if ws is None:
+        ws = workspace(shape, OP_BACKWARD, dev)
+    _check(_lib.bsga_attn_backward(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(lse), _ptr(d_o), _ptr(row_ptr), _ptr(col_idx),
+                                   *[_ptr(g) for g in grads], _ws_ptr(ws), _ws_len(ws),
+                                   _stream(dev)), "bsga_attn_backward")
+    return tuple(grads)
 
 
 def pooled_specials_shape(shape: LayerShape) -> LayerShape:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsga.so")
 SOURCES = ["bsga_api.cpp", "budget.cpp", "predict.hip", "select.hip", "probe.hip",
-           "metrics.hip", "attention.hip"]
+           "metrics.hip", "attention.hip", "backward.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -41,7 +41,8 @@ def hipcc() -> str:
 # (masked scores are -inf, not NaN), so they run with the IEEE mode bit off,
 # which lets float max chains fold into v_max3 without canonicalising every
 # MFMA result first.
-EXTRA = {"attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+EXTRA = {"attention.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+         "backward.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

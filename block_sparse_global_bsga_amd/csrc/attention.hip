@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "bsga_internal.hpp"
+#include "tile_common.hpp"
 
 namespace bsga {
 
@@ -78,30 +79,11 @@ struct AttnArgs {
   int tiles_per_split;
 };
 
-constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
 // A tile is exponentiated against a stale running max as long as its exact
 // max is at most 64 log2 units above it: weights up to 2^64 are exact enough
 // in float32 and bf16, and sums over any sequence length stay far below
 // float32 overflow.
 constexpr float kLazySlack = 64.f;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline int pi_row(int i) {
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-// LDS swizzles (16-byte chunk index XOR a row function) so that the MFMA
-// operand reads touch distinct banks.
-__device__ inline int swz_k(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 1); }
-template <int KT>
-__device__ inline int swz_v(int d) {
-  if constexpr (KT == 128) return d & 15;
-  else return ((d >> 1) & 7) ^ ((d & 1) << 2);
-}
 
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).

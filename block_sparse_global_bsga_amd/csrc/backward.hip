@@ -1,0 +1,600 @@
+// Backward of the layer's attention for a fixed block mask (the outlook of
+// "Block-Sparse Global Attention for Efficient Multi-View Geometry
+// Transformers": sparse attention inside training).  The mask is the one the
+// forward used: patch queries see the patch tokens of their kept blocks and
+// every special token; special queries see every token.  The block selection
+// is not differentiated.
+//
+// With the forward's LSE, per allowed (query, key): P = exp(q.k/8 - LSE),
+// dP = dO . v, D = dO . O (per query), dS = P (dP - D), and
+//   dQ = sum_k dS k / 8,  dK = sum_q dS q / 8,  dV = sum_q P dO.
+//
+// Layout: every operand is first packed (the forward's packed order: patch
+// tokens, pad, special tokens, pad) both as rows [H][Ntot][64] and, where a
+// product contracts over tokens, transposed [H][64][Ntot], so that tiles
+// stream into LDS with direct-to-LDS loads exactly as in the forward.
+//
+// dq_kernel (query-major, over the CSR rows): per wave 32 queries with Q and
+//   dO rows in registers; per key tile S^T = K Q^T and dP^T = V dO^T (K, V
+//   rows from LDS), dS^T in the accumulator layout, dQ^T += K^T dS^T with dS^T
+//   taken straight from the accumulators as the B operand (K row permutation
+//   pi, as in the forward).
+// dkdv_kernel (key-major, over the transposed CSR): per wave 32 keys with K
+//   and V rows in registers; per query tile S = Q K^T and dP = dO V^T (Q, dO
+//   rows from LDS, row permutation pi), then dV^T += dO^T P and
+//   dK^T += Q^T dS from the accumulators.
+#include "bsga_internal.hpp"
+#include "tile_common.hpp"
+
+namespace bsga {
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------------------
+// Packing: rows and/or transposed copies of one [H][N][64] tensor in packed
+// order, 64 tokens per workgroup (zeros for padding).
+__global__ __launch_bounds__(256) void bwd_pack_kernel(const uint4* __restrict__ x,
+                                                       uint4* __restrict__ rows,
+                                                       uint4* __restrict__ cols, Dims d) {
+  __shared__ uint16_t sv[64][66];
+  const int kp0 = blockIdx.x * 64, h = blockIdx.y, T = threadIdx.x;
+  const size_t src_head = (size_t)h * d.n * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int row = c >> 3, ch = c & 7;
+    const int tok = packed_token(kp0 + row, d);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) v = x[src_head + (size_t)tok * 8 + ch];
+    if (rows) rows[((size_t)h * d.ntot_pad + kp0 + row) * 8 + ch] = v;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[row][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xffff);
+      sv[row][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  if (!cols) return;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int dr = c >> 3, kc = c & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)sv[8 * kc + 2 * e][dr] | ((uint32_t)sv[8 * kc + 2 * e + 1][dr] << 16);
+    cols[(((size_t)h * 64 + dr) * d.ntot_pad + kp0) / 8 + kc] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Per packed row: lse2 = LSE * log2(e) (+inf for padding, so every weight of
+// a padding row is 0) and D = dO . O in float32 (0 for padding).  dq_kernel
+// overwrites D for every row of its query tiles with sum_k P dP; rows no
+// query tile covers are padding and keep 0.
+__global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restrict__ o,
+                                                           const uint4* __restrict__ d_o,
+                                                           const float* __restrict__ lse,
+                                                           float* __restrict__ lse2,
+                                                           float* __restrict__ dd, Dims d) {
+  const int h = blockIdx.y, T = threadIdx.x, ch = T & 7;
+  const int kp = blockIdx.x * 32 + (T >> 3);  // 32 rows per workgroup, 8 lanes per row
+  const int tok = packed_token(kp, d);
+  float s = 0.f;
+  if (tok >= 0) {
+    const size_t at = ((size_t)h * d.n + tok) * 8 + ch;
+    const uint4 a = o[at], b = d_o[at];
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(wb[e] << 16), s);
+      s = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(wb[e] & 0xffff0000u), s);
+    }
+  }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (ch == 0) {
+    const size_t r = (size_t)h * d.ntot_pad + kp;
+    dd[r] = s;
+    lse2[r] = tok >= 0 ? lse[(size_t)h * d.n + tok] * 1.4426950408889634f : INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed CSR: for key block j of head h, the query blocks i (ascending)
+// whose kept list holds j.
+__device__ inline bool row_has(const int32_t* __restrict__ cols, int n, int j) {
+  int lo = 0, hi = n;  // sorted ascending
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (cols[mid] < j) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && cols[lo] == j;
+}
+
+__global__ __launch_bounds__(256) void csr_t_count_kernel(const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          Dims d, int32_t* __restrict__ count) {
+  __shared__ int red[4];
+  const int j = blockIdx.x, h = blockIdx.y, T = threadIdx.x;
+  int c = 0;
+  for (int i = T; i < d.B; i += 256) {
+    const int r = h * d.B + i;
+    const int a = row_ptr[r];
+    c += row_has(col_idx + a, max(0, min(row_ptr[r + 1] - a, d.B)), j);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if ((T & 63) == 0) red[T >> 6] = c;
+  __syncthreads();
+  if (T == 0) count[h * d.B + j] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void csr_t_fill_kernel(const int32_t* __restrict__ row_ptr,
+                                                         const int32_t* __restrict__ col_idx,
+                                                         const int32_t* __restrict__ t_ptr, Dims d,
+                                                         int32_t* __restrict__ t_list) {
+  __shared__ int wave_tot[4];
+  const int j = blockIdx.x, h = blockIdx.y, T = threadIdx.x;
+  const int per = (d.B + 255) / 256;
+  const int lo = min(d.B, T * per), hi = min(d.B, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int r = h * d.B + i, a = row_ptr[r];
+    local += row_has(col_idx + a, max(0, min(row_ptr[r + 1] - a, d.B)), j);
+  }
+  const int lane = T & 63, w = T >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_tot[w] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int u = 0; u < w; ++u) run += wave_tot[u];
+  int32_t* out = t_list + t_ptr[h * d.B + j];
+  for (int i = lo; i < hi; ++i) {
+    const int r = h * d.B + i, a = row_ptr[r];
+    if (row_has(col_idx + a, max(0, min(row_ptr[r + 1] - a, d.B)), j)) out[run++] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS tile loads of NW waves.  A row tile (ROWS x 64 bf16) is ROWS*8
+// chunks, chunk (row, pc) filled from logical chunk pc ^ swz_k(row); a
+// transposed tile (64 dims x T tokens) is 64 * T/8 chunks, chunk (dim, pc)
+// from logical chunk pc ^ swz_v<T>(dim).
+template <int ROWS, int NW>
+__device__ inline void load_rows(const char* head_base, int row0, u32x4* lds, int w, int lane) {
+  constexpr int LPW = ROWS * 8 / (64 * NW);
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = LPW * w + i;
+    const int row = 8 * blk + (lane >> 3), pc = lane & 7;
+    const char* src = head_base + (size_t)(row0 + row) * 128 + 16 * (pc ^ swz_k(row));
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
+                                     0, 0);
+  }
+}
+template <int T, int NW>
+__device__ inline void load_cols(const char* head_base, uint32_t row_bytes, int col0, u32x4* lds,
+                                 int w, int lane) {
+  constexpr int LPW = T * 8 / (64 * NW);
+  constexpr int CPR = T / 8;       // chunks per dim row
+  constexpr int RPB = 64 / CPR;    // dim rows per 64-chunk block
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = LPW * w + i;
+    const int dim = RPB * blk + lane / CPR, pc = lane % CPR;
+    const char* src = head_base + (size_t)dim * row_bytes + (size_t)col0 * 2 + 16 * (pc ^ swz_v<T>(dim));
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
+                                     0, 0);
+  }
+}
+
+struct BwdArgs {
+  const uint16_t* qp;   // packed rows
+  const uint16_t* qt;   // packed transposed
+  const uint16_t* dop;
+  const uint16_t* dot;
+  const uint16_t* kp;
+  const uint16_t* kt;
+  const uint16_t* vp;
+  const float* lse2;    // [H][Ntot]
+  const float* dd;      // [H][Ntot] D per packed row, read by dkdv_kernel
+  float* dd_out;        // the same array, written by dq_kernel
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* t_ptr;
+  const int32_t* t_list;
+  float* dq;            // [H][N][64] token order
+  float* dk;
+  float* dv;
+  Dims d;
+  int n_items;
+};
+
+// ---------------------------------------------------------------------------
+// dQ: QT queries per workgroup (one patch block, or a tile of special
+// queries), KT-key tiles: the kept blocks (TPB tiles each) then the special
+// tiles for patch queries, every tile for special queries.
+template <int QT, int KT>
+__global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+    BwdArgs a) {
+  constexpr int NW = QT / 32, NS = KT / 32, VROW = KT / 8, KCH = 8 * KT, TPB = QT / KT;
+  __shared__ u32x4 smem[2 * 3 * KCH];  // slot s: K rows, V rows, K^T
+  const Dims& d = a.d;
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, a.n_items));
+  if (item < 0) return;
+  const int T = threadIdx.x, lane = T & 63;
+  const int w = __builtin_amdgcn_readfirstlane(T >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int q_tiles = d.B + d.ns_pad / QT;
+  const int h = __builtin_amdgcn_readfirstlane(item / q_tiles);
+  const int qi = __builtin_amdgcn_readfirstlane(item - h * q_tiles);
+  const bool patch_q = qi < d.B;
+  const int qp0 = patch_q ? qi * QT : d.np_pad + (qi - d.B) * QT;
+  int nt, nt_csr = 0;
+  const int32_t* cols = nullptr;
+  if (patch_q) {
+    const int r0 = a.row_ptr[h * d.B + qi];
+    cols = a.col_idx + r0;
+    nt_csr = max(0, min(a.row_ptr[h * d.B + qi + 1] - r0, d.B));
+    nt = nt_csr * TPB + d.ns_pad / KT;
+  } else {
+    nt = d.ntot_pad / KT;
+  }
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
+  auto tile_raw = [&](int n) -> int { return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0; };
+  auto tile_kp0 = [&](int n, int raw) -> int {
+    raw = __builtin_amdgcn_readfirstlane(raw);
+    if (!patch_q) return n * KT;
+    const int nb = nt_csr * TPB;
+    if (n >= nb) return d.np_pad + (n - nb) * KT;
+    return min(max(raw, 0), d.B - 1) * QT + (n % TPB) * KT;
+  };
+  auto tile_valid = [&](int kp0) -> int {
+    return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
+  };
+
+  // this wave's 32 query rows: Q and dO fragments, lse2, D
+  const int qrow = qp0 + 32 * w + l32;
+  bf16x8 qop[4], dop[4];
+  {
+    const u32x4* sq = (const u32x4*)(a.qp + ((size_t)h * d.ntot_pad + qrow) * kHeadDim) + 4 * hh;
+    const u32x4* so = (const u32x4*)(a.dop + ((size_t)h * d.ntot_pad + qrow) * kHeadDim) + 4 * hh;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      qop[m] = as_bf16x8(sq[m]);
+      dop[m] = as_bf16x8(so[m]);
+    }
+  }
+  const float lse2 = a.lse2[(size_t)h * d.ntot_pad + qrow];
+
+  const char* kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * 128;
+  const char* vbase = (const char*)a.vp + (size_t)h * d.ntot_pad * 128;
+  const uint32_t trow = (uint32_t)d.ntot_pad * 2;
+  const char* ktbase = (const char*)a.kt + (size_t)h * 64 * trow;
+  auto issue = [&](int kp0, int slot, bool with_kt) {
+    u32x4* base = smem + slot * 3 * KCH;
+    load_rows<KT, NW>(kbase, kp0, base, w, lane);
+    load_rows<KT, NW>(vbase, kp0, base + KCH, w, lane);
+    if (with_kt) load_cols<KT, NW>(ktbase, trow, kp0, base + 2 * KCH, w, lane);
+  };
+
+  // Two sweeps over the key tiles.  The first accumulates D = sum_k P dP,
+  // which equals dO . O for this query, from the same float32 P and dP the
+  // second sweep uses, so that the dS of a query sum to zero up to float32
+  // rounding (D from the stored bf16 O would not, and the gradients of a
+  // peaked softmax are exactly such small differences).  The second sweep
+  // forms dS = P (dP - D) and feeds it to the dQ product as a bf16 pair
+  // hi + lo (16 significant bits), for the same reason.
+  f32x16 g0 = {}, g1 = {};  // dQ^T: dims 0-31 and 32-63 x the wave's 32 queries
+  float d_lane = 0.f, dq_d = 0.f;
+  for (int sweep = 0; sweep < 2; ++sweep) {
+    const bool second = sweep == 1;
+    int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
+    if (nt > 0) issue(tile_kp0(0, raw_cur), 0, second);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int n = 0; n < nt; ++n) {
+      const int slot = n & 1;
+      if (n + 1 < nt) issue(tile_kp0(n + 1, raw_nxt), slot ^ 1, second);
+      const int raw_after = tile_raw(n + 2);
+      const u32x4* kt = smem + slot * 3 * KCH;
+      const u32x4* vt = kt + KCH;
+      const u32x4* ktt = kt + 2 * KCH;
+      const int valid = tile_valid(tile_kp0(n, raw_cur));
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int R = 32 * t + pi_row(l32);
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt[c]), qop[m], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vt[c]), dop[m], dp, 0, 0, 0);
+        }
+        if (!second) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+            const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
+            d_lane = fmaf(key < valid ? p : 0.f, dp[r], d_lane);
+          }
+          continue;
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 e8, rem;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h2 + e;
+            const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
+            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+            e8[e] = key < valid ? p * (dp[r] - dq_d) : 0.f;
+          }
+          const bf16x8 ds_hi = __builtin_convertvector(e8, bf16x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)ds_hi[e];
+          const bf16x8 ds_lo = __builtin_convertvector(rem, bf16x8);
+          const int ch = 4 * t + 2 * h2 + hh;
+          const bf16x8 k0 = as_bf16x8(ktt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
+          const bf16x8 k1 = as_bf16x8(ktt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+          g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_hi, g0, 0, 0, 0);
+          g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_hi, g1, 0, 0, 0);
+          g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
+          g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_lo, g1, 0, 0, 0);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      raw_cur = raw_nxt;
+      raw_nxt = raw_after;
+    }
+    if (!second) {
+      dq_d = xor32_sum(d_lane);  // lanes l and l + 32 hold the same query
+      if (hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = dq_d;
+    }
+  }
+  const int tok = packed_token(qrow, d);
+  if (tok < 0) return;
+  float* out = a.dq + ((size_t)h * d.n + tok) * kHeadDim;
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa) {
+    *(f32x4*)(out + 8 * aa + 4 * hh) =
+        f32x4{g0[4 * aa], g0[4 * aa + 1], g0[4 * aa + 2], g0[4 * aa + 3]} * 0.125f;
+    *(f32x4*)(out + 32 + 8 * aa + 4 * hh) =
+        f32x4{g1[4 * aa], g1[4 * aa + 1], g1[4 * aa + 2], g1[4 * aa + 3]} * 0.125f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: KT keys per workgroup (one patch block, or a tile of special keys),
+// QT-query tiles: for a patch key block the query blocks that keep it (from
+// the transposed CSR, QPB tiles each) then every special query tile; for
+// special keys every query tile.
+template <int KT, int QT>
+__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64, KT / 64))) void dkdv_kernel(
+    BwdArgs a, int qpb) {
+  constexpr int NW = KT / 32, NS = QT / 32, VROW = QT / 8, QCH = 8 * QT;
+  static_assert(QT == 64 && NW >= 2, "one 64-lane load per statistics row");
+  // slot s: Q rows, dO rows, Q^T, dO^T, then lse2 and D
+  __shared__ u32x4 smem[2 * 4 * QCH];
+  __shared__ float stats[2][2][QT];
+  const Dims& d = a.d;
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, a.n_items));
+  if (item < 0) return;
+  const int T = threadIdx.x, lane = T & 63;
+  const int w = __builtin_amdgcn_readfirstlane(T >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int k_tiles = d.B + d.ns_pad / KT;
+  const int h = __builtin_amdgcn_readfirstlane(item / k_tiles);
+  const int kj = __builtin_amdgcn_readfirstlane(item - h * k_tiles);
+  const bool patch_k = kj < d.B;
+  const int kp0 = patch_k ? kj * KT : d.np_pad + (kj - d.B) * KT;
+  int nt, nt_t = 0;
+  const int32_t* qlist = nullptr;
+  if (patch_k) {
+    const int r0 = a.t_ptr[h * d.B + kj];
+    qlist = a.t_list + r0;
+    nt_t = max(0, min(a.t_ptr[h * d.B + kj + 1] - r0, d.B));
+    nt = nt_t * qpb + d.ns_pad / QT;
+  } else {
+    nt = d.ntot_pad / QT;
+  }
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  nt_t = __builtin_amdgcn_readfirstlane(nt_t);
+  auto tile_raw = [&](int n) -> int { return nt_t > 0 ? qlist[min(n / qpb, nt_t - 1)] : 0; };
+  auto tile_qp0 = [&](int n, int raw) -> int {
+    raw = __builtin_amdgcn_readfirstlane(raw);
+    if (!patch_k) return n * QT;
+    const int nb = nt_t * qpb;
+    if (n >= nb) return d.np_pad + (n - nb) * QT;
+    return min(max(raw, 0), d.B - 1) * (qpb * QT) + (n % qpb) * QT;
+  };
+
+  // this wave's 32 keys: K and V fragments
+  const int krow = kp0 + 32 * w + l32;
+  bf16x8 kop[4], vop[4];
+  {
+    const u32x4* sk = (const u32x4*)(a.kp + ((size_t)h * d.ntot_pad + krow) * kHeadDim) + 4 * hh;
+    const u32x4* sv = (const u32x4*)(a.vp + ((size_t)h * d.ntot_pad + krow) * kHeadDim) + 4 * hh;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      kop[m] = as_bf16x8(sk[m]);
+      vop[m] = as_bf16x8(sv[m]);
+    }
+  }
+
+  const size_t hrow = (size_t)h * d.ntot_pad;
+  const char* qbase = (const char*)a.qp + hrow * 128;
+  const char* obase = (const char*)a.dop + hrow * 128;
+  const uint32_t trow = (uint32_t)d.ntot_pad * 2;
+  const char* qtbase = (const char*)a.qt + (size_t)h * 64 * trow;
+  const char* otbase = (const char*)a.dot + (size_t)h * 64 * trow;
+  auto issue = [&](int qp0, int slot) {
+    u32x4* base = smem + slot * 4 * QCH;
+    load_rows<QT, NW>(qbase, qp0, base, w, lane);
+    load_rows<QT, NW>(obase, qp0, base + QCH, w, lane);
+    load_cols<QT, NW>(qtbase, trow, qp0, base + 2 * QCH, w, lane);
+    load_cols<QT, NW>(otbase, trow, qp0, base + 3 * QCH, w, lane);
+    // lse2 and D of the tile's 64 queries: one 4-byte direct-to-LDS load per
+    // lane, issued by waves 0 and 1 (no register round trip, no extra wait)
+    if (w < 2)
+      __builtin_amdgcn_global_load_lds((const void*)((w == 0 ? a.lse2 : a.dd) + hrow + qp0 + lane),
+                                       (lds_void*)&stats[slot][w][0], 4, 0, 0);
+  };
+
+  f32x16 v0 = {}, v1 = {}, k0 = {}, k1 = {};  // dV^T, dK^T: dims x the wave's 32 keys
+  int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
+  if (nt > 0) issue(tile_qp0(0, raw_cur), 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int n = 0; n < nt; ++n) {
+    const int slot = n & 1;
+    if (n + 1 < nt) issue(tile_qp0(n + 1, raw_nxt), slot ^ 1);
+    const int raw_after = tile_raw(n + 2);
+    const u32x4* qr = smem + slot * 4 * QCH;
+    const u32x4* orr = qr + QCH;
+    const u32x4* qtt = qr + 2 * QCH;
+    const u32x4* ott = qr + 3 * QCH;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int R = 32 * t + pi_row(l32);
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qr[c]), kop[m], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(orr[c]), vop[m], dp, 0, 0, 0);
+      }
+      // accumulator row i of this lane holds query 32t + pi(i), i = 8(r/4) + 4hh + r%4
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x8 p8, s8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * h2 + e;
+          const int qq = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+          const float p = fast_exp2(fmaf(s[r], kScaleLog2, -stats[slot][0][qq]));
+          p8[e] = p;
+          s8[e] = p * (dp[r] - stats[slot][1][qq]);
+        }
+        // P and dS enter the products as bf16 pairs hi + lo: dV and dK of a
+        // key sum thousands of weighted rows, and a single bf16 rounding of
+        // each weight would dominate their error
+        const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+        const bf16x8 sb = __builtin_convertvector(s8, bf16x8);
+        f32x8 prem, rem;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          prem[e] = p8[e] - (float)pb[e];
+          rem[e] = s8[e] - (float)sb[e];
+        }
+        const bf16x8 pl = __builtin_convertvector(prem, bf16x8);
+        const bf16x8 sl = __builtin_convertvector(rem, bf16x8);
+        const int ch = 4 * t + 2 * h2 + hh;
+        const bf16x8 o0 = as_bf16x8(ott[l32 * VROW + (ch ^ swz_v<QT>(l32))]);
+        const bf16x8 o1 = as_bf16x8(ott[(32 + l32) * VROW + (ch ^ swz_v<QT>(32 + l32))]);
+        const bf16x8 q0 = as_bf16x8(qtt[l32 * VROW + (ch ^ swz_v<QT>(l32))]);
+        const bf16x8 q1 = as_bf16x8(qtt[(32 + l32) * VROW + (ch ^ swz_v<QT>(32 + l32))]);
+        v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pb, v0, 0, 0, 0);
+        v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pb, v1, 0, 0, 0);
+        v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pl, v0, 0, 0, 0);
+        v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pl, v1, 0, 0, 0);
+        k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sb, k0, 0, 0, 0);
+        k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sb, k1, 0, 0, 0);
+        k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sl, k0, 0, 0, 0);
+        k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sl, k1, 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    raw_cur = raw_nxt;
+    raw_nxt = raw_after;
+  }
+  const int tok = packed_token(krow, d);
+  if (tok < 0) return;
+  float* ok = a.dk + ((size_t)h * d.n + tok) * kHeadDim;
+  float* ov = a.dv + ((size_t)h * d.n + tok) * kHeadDim;
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa) {
+    *(f32x4*)(ok + 8 * aa + 4 * hh) =
+        f32x4{k0[4 * aa], k0[4 * aa + 1], k0[4 * aa + 2], k0[4 * aa + 3]} * 0.125f;
+    *(f32x4*)(ok + 32 + 8 * aa + 4 * hh) =
+        f32x4{k1[4 * aa], k1[4 * aa + 1], k1[4 * aa + 2], k1[4 * aa + 3]} * 0.125f;
+    *(f32x4*)(ov + 8 * aa + 4 * hh) = f32x4{v0[4 * aa], v0[4 * aa + 1], v0[4 * aa + 2], v0[4 * aa + 3]};
+    *(f32x4*)(ov + 32 + 8 * aa + 4 * hh) =
+        f32x4{v1[4 * aa], v1[4 * aa + 1], v1[4 * aa + 2], v1[4 * aa + 3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+size_t backward_workspace(const Dims& d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t arr = up((size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t));
+  return 7 * arr + 2 * up((size_t)d.H * d.ntot_pad * sizeof(float)) +
+         up(((size_t)d.H * d.B + 1) * sizeof(int32_t)) +   // t_ptr
+         up((size_t)d.H * d.B * sizeof(int32_t)) +         // counts
+         up((size_t)d.H * d.B * d.B * sizeof(int32_t));   // t_list
+}
+
+hipError_t launch_scan_counts(const int32_t* counts, int rows, int32_t* row_ptr, hipStream_t st);
+
+hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const float* lse, const uint16_t* d_o,
+                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
+                           float* dv, void* ws, hipStream_t st) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t arr = up((size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t));
+  char* p = (char*)ws;
+  uint16_t* qp = (uint16_t*)p; p += arr;
+  uint16_t* qt = (uint16_t*)p; p += arr;
+  uint16_t* dop = (uint16_t*)p; p += arr;
+  uint16_t* dot = (uint16_t*)p; p += arr;
+  uint16_t* kp = (uint16_t*)p; p += arr;
+  uint16_t* kt = (uint16_t*)p; p += arr;
+  uint16_t* vp = (uint16_t*)p; p += arr;
+  float* lse2 = (float*)p; p += up((size_t)d.H * d.ntot_pad * sizeof(float));
+  float* dd = (float*)p; p += up((size_t)d.H * d.ntot_pad * sizeof(float));
+  int32_t* t_ptr = (int32_t*)p; p += up(((size_t)d.H * d.B + 1) * sizeof(int32_t));
+  int32_t* counts = (int32_t*)p; p += up((size_t)d.H * d.B * sizeof(int32_t));
+  int32_t* t_list = (int32_t*)p;
+
+  const dim3 pg(d.ntot_pad / 64, d.H);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)q, (uint4*)qp, (uint4*)qt, d);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)d_o, (uint4*)dop, (uint4*)dot, d);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)k, (uint4*)kp, (uint4*)kt, d);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)v, (uint4*)vp, nullptr, d);
+  bwd_rowstats_kernel<<<dim3(d.ntot_pad / 32, d.H), 256, 0, st>>>(
+      (const uint4*)o, (const uint4*)d_o, lse, lse2, dd, d);
+  csr_t_count_kernel<<<dim3(d.B, d.H), 256, 0, st>>>(row_ptr, col_idx, d, counts);
+  hipError_t e = launch_scan_counts(counts, d.H * d.B, t_ptr, st);
+  if (e != hipSuccess) return e;
+  csr_t_fill_kernel<<<dim3(d.B, d.H), 256, 0, st>>>(row_ptr, col_idx, t_ptr, d, t_list);
+
+  BwdArgs a = {};
+  a.qp = qp; a.qt = qt; a.dop = dop; a.dot = dot; a.kp = kp; a.kt = kt; a.vp = vp;
+  a.lse2 = lse2; a.dd = dd; a.dd_out = dd; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.t_ptr = t_ptr; a.t_list = t_list; a.dq = dq; a.dk = dk; a.dv = dv; a.d = d;
+  if (d.b == 128) {
+    a.n_items = d.H * (d.B + d.ns_pad / 128);
+    dq_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+    a.n_items = d.H * (d.B + d.ns_pad / 128);
+    dkdv_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
+  } else {
+    a.n_items = d.H * (d.B + d.ns_pad / 64);
+    dq_kernel<64, 64><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
+    a.n_items = d.H * (d.B + d.ns_pad / 64);
+    dkdv_kernel<64, 64><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 1);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsga

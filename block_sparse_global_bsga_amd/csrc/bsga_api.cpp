@@ -78,6 +78,7 @@ size_t ws_pack(const Dims& d) { return up(pack_bytes(d)); }
 size_t ws_special(const Dims& d) { return up(special_workspace(d)); }
 size_t ws_probe(const Dims& d) { return up(probe_workspace(d)); }
 size_t ws_nmse(const Dims& d) { return up(nmse_workspace(d)); }
+size_t ws_backward(const Dims& d) { return up(backward_workspace(d)); }
 
 size_t ws_for(const Dims& d, int op) {
   switch (op) {
@@ -89,6 +90,7 @@ size_t ws_for(const Dims& d, int op) {
     case BSGA_OP_SPECIAL_DENSE_PACKED: return ws_special(d);
     case BSGA_OP_PROBE_SELECT: return ws_probe(d);
     case BSGA_OP_NMSE: return ws_nmse(d);
+    case BSGA_OP_BACKWARD: return ws_backward(d);
     case BSGA_OP_LAYER: {
       size_t m = ws_predict(d);
       if (ws_select(d) > m) m = ws_select(d);
@@ -191,7 +193,7 @@ int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries) {
 
 int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes) {
   BSGA_TRY(check_shape(shape));
-  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_NMSE)
+  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_BACKWARD)
     return BSGA_ERR_INVALID_ARG;
   *bytes = ws_for(make_dims(*shape), op);
   return BSGA_OK;
@@ -253,6 +255,27 @@ int bsga_nmse(const bsga_shape* shape, const uint16_t* o_ref, const uint16_t* o,
   BSGA_TRY(check_ptr(nmse, 8));
   BSGA_TRY(check_ws(d, BSGA_OP_NMSE, ws, ws_bytes));
   return hip_status(launch_nmse(d, o_ref, o, nmse, ws, (hipStream_t)stream));
+}
+
+int bsga_attn_backward(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const uint16_t* o, const float* lse,
+                       const uint16_t* d_o, const int32_t* row_ptr, const int32_t* col_idx,
+                       float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_select_shape(d));
+  BSGA_TRY(check_qkv(q, k, v));
+  BSGA_TRY(check_ptr(o, 16));
+  BSGA_TRY(check_ptr(d_o, 16));
+  BSGA_TRY(check_ptr(lse, 4));
+  BSGA_TRY(check_ptr(row_ptr, 4));
+  BSGA_TRY(check_ptr(col_idx, 4));
+  BSGA_TRY(check_ptr(dq, 16));
+  BSGA_TRY(check_ptr(dk, 16));
+  BSGA_TRY(check_ptr(dv, 16));
+  BSGA_TRY(check_ws(d, BSGA_OP_BACKWARD, ws, ws_bytes));
+  return hip_status(launch_backward(d, q, k, v, o, lse, d_o, row_ptr, col_idx, dq, dk, dv, ws,
+                                    (hipStream_t)stream));
 }
 
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,

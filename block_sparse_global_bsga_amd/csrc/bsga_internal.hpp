@@ -127,6 +127,12 @@ size_t nmse_workspace(const Dims& d);
 hipError_t launch_nmse(const Dims& d, const uint16_t* ref, const uint16_t* out, double* result,
                        void* ws, hipStream_t st);
 
+size_t backward_workspace(const Dims& d);
+hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const float* lse, const uint16_t* d_o,
+                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
+                           float* dv, void* ws, hipStream_t st);
+
 size_t pack_bytes(const Dims& d);  // packed K and V^T
 hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v,
                        uint16_t* kp, uint16_t* vt, hipStream_t st);

@@ -188,4 +188,9 @@ hipError_t launch_select(const Dims& d, const float* probs, const SelectParams& 
   return hipGetLastError();
 }
 
+hipError_t launch_scan_counts(const int32_t* counts, int rows, int32_t* row_ptr, hipStream_t st) {
+  scan_counts_kernel<<<1, 1024, 0, st>>>(counts, rows, row_ptr);
+  return hipGetLastError();
+}
+
 }  // namespace bsga

@@ -70,7 +70,8 @@ typedef enum bsga_op {
   BSGA_OP_LAYER = 5,
   BSGA_OP_SPECIAL_DENSE_PACKED = 6,
   BSGA_OP_PROBE_SELECT = 7,
-  BSGA_OP_NMSE = 8
+  BSGA_OP_NMSE = 8,
+  BSGA_OP_BACKWARD = 9
 } bsga_op;
 
 /* Shape of one global-attention layer.  head_dim must be 64; block (b) must
@@ -227,6 +228,31 @@ int bsga_dense_attn(const bsga_shape* shape, const uint16_t* q,
 int bsga_nmse(const bsga_shape* shape, const uint16_t* o_ref, const uint16_t* o,
               double* nmse, void* workspace, size_t workspace_bytes,
               void* stream);
+
+/* Backward of the layer's attention for a fixed mask ([BSGA] outlook:
+ * sparse attention inside training; the block selection is not
+ * differentiated).  For the output O of bsga_layer (patch queries over their
+ * kept patch blocks and every special key, special queries over every key),
+ * given dO = dL/dO, writes dQ, dK, dV = dL/dQ, dL/dK, dL/dV:
+ *   P = exp(q.k / 8 - LSE),  dS = P (dO.v - dO.O),
+ *   dQ = sum_k dS k / 8,  dK = sum_q dS q / 8,  dV = sum_q P dO.
+ *   q, k, v, o, d_o: [H][N][64] bf16 (o and lse as written by the forward
+ *     with this mask); lse: [H][N] float32; row_ptr/col_idx: the mask (as
+ *     returned by bsga_select or bsga_probe_select).
+ *   dq, dk, dv: [H][N][64] float32 outputs, 16-byte aligned, fully written.
+ *   workspace: bsga_workspace_bytes(BSGA_OP_BACKWARD) (packed operands,
+ *     row statistics and the transposed mask).
+ * bf16 MFMA products with float32 accumulation; P and dS enter them as bf16
+ * pairs hi + lo, and D = dO . O is recomputed as sum_k P dP from the same
+ * float32 P and dP (the stored bf16 O is not used for it).  No atomics: dQ
+ * is accumulated per query tile over the mask's rows, dK and dV per key tile
+ * over its transpose (deterministic). */
+int bsga_attn_backward(const bsga_shape* shape, const uint16_t* q,
+                       const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                       const float* lse, const uint16_t* d_o,
+                       const int32_t* row_ptr, const int32_t* col_idx,
+                       float* dq, float* dk, float* dv, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Packed K/V: the layout the attention kernels stream.  Keys are listed in
  * "packed order" — the N_p patch tokens in patch order, zero rows up to the

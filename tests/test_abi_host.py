@@ -69,7 +69,8 @@ def test_capacity_and_workspace_sizes():
     # per-head NMSE: one float64 pair per head and chunk of 1024 rows
     assert bsga.workspace_bytes(shape, bsga.OP_NMSE) >= 16 * 43 * 16
     out = ctypes.c_size_t()
-    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_NMSE + 1,
+    assert bsga.workspace_bytes(shape, bsga.OP_BACKWARD) >= 7 * 16 * 44032 * 128
+    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_BACKWARD + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 
 
