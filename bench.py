@@ -28,6 +28,10 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HEAD_DIM = 64
+# algorithmic flops of the backward per computed (query, key) entry: the five
+# products S = QK^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q, dQ += dS K,
+# 2 * d_h each (recomputation and hi + lo splits not counted)
+BWD_FLOP_PER_ENTRY = 10 * HEAD_DIM
 
 
 def parse():
@@ -48,7 +52,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "attn_patch_rows_32f_hbm_traffic.txt")
-KERNEL_SOURCES = ("attention.hip", "bsga_internal.hpp")
+KERNEL_SOURCES = ("attention.hip", "tile_common.hpp", "bsga_internal.hpp")
 
 
 def kernel_source_digest() -> str:
@@ -305,6 +309,23 @@ def main():
                                               if x.head_types[h] == t]))
                              for t in sorted(set(x.head_types))}
         del layer_pool
+        # backward of the layer's attention for the standard layer's mask
+        d_o = up(synth.fp32_to_bf16_bits(np.random.default_rng(5).standard_normal(
+            (cfg.heads, n, HEAD_DIM), dtype=np.float32)))
+        ws_bwd = bsga.workspace(shape, bsga.OP_BACKWARD, dev)
+        grads = [torch.empty((cfg.heads, n, HEAD_DIM), dtype=torch.float32, device=dev)
+                 for _ in range(3)]
+        bwd_ms, _ = timed(lambda _ev: bsga.attn_backward(
+            shape, q, k, v, layer_std.o, layer_std.lse, d_o, layer_std.row_ptr,
+            layer_std.col_idx, dq=grads[0], dk=grads[1], dv=grads[2], ws=ws_bwd),
+            max(3, args.steps // 2), 2)
+        rpb = layer_std.row_ptr.cpu().numpy()
+        ppb, spb = computed_entries(rpb, layer_std.col_idx[:int(rpb[-1])].cpu().numpy(),
+                                    cfg.n_patch, cfg.block, cfg.heads, cfg.n_special)
+        bwd_tflops = BWD_FLOP_PER_ENTRY * (ppb + spb) / (bwd_ms * 1e-3) / 1e12
+        print(f"# backward {bwd_ms:.3f} ms ({bwd_tflops:.0f} TFLOP/s)", file=sys.stderr,
+              flush=True)
+        del grads, ws_bwd, d_o
         extras = {
             "probe_topk": {"topk": topk, "select_ms": round(probe_parts[0], 4),
                            "select_GB/s": round(probe_bytes / (probe_parts[0] * 1e-3) / 1e9, 1),
@@ -313,6 +334,10 @@ def main():
             "nmse_vs_dense_by_head_type": by_type,
             "nmse_kernel": {"ms": round(nmse_ms, 4),
                             "GB/s": round(2 * tok_bytes * n / (nmse_ms * 1e-3) / 1e9, 1)},
+            "backward": {"ms": round(bwd_ms, 4),
+                         "flop_per_entry": BWD_FLOP_PER_ENTRY,
+                         "TFLOP/s": round(bwd_tflops, 1),
+                         "frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4)},
             "dense_ms": round(dense_ms, 4),
             "speedup_vs_dense": round(dense_ms / ms, 3),
             "bsga_layer_call_ms": round(layer_call_ms, 4),
