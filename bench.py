@@ -270,6 +270,30 @@ def main():
                                     cfg.block, cfg.heads, cfg.n_special)
         print(f"# dense {dense_ms:.3f} ms; bsga_layer call {layer_call_ms:.3f} ms; "
               f"tau=0: {ms0:.3f} ms", file=sys.stderr, flush=True)
+        # per-step latency, median of single steps: warm caches, and with 512 MB
+        # written between steps so that neither L2 nor MALL (256 MB) still
+        # holds the layer's K/V
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def step_latencies(flushed, reps):
+            out = []
+            for i in range(reps):
+                if flushed:
+                    flush.fill_(i & 255)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step(cfg.rho, cfg.tau)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                out.append(e0.elapsed_time(e1))
+            return float(np.median(out))
+
+        lat_reps = max(5, args.steps)
+        warm_median = step_latencies(False, lat_reps)
+        flushed_median = step_latencies(True, lat_reps)
+        del flush
+        print(f"# single-step median: warm {warm_median:.3f} ms, flushed {flushed_median:.3f} ms",
+              file=sys.stderr, flush=True)
         # query-probe Top-K lists (1 % of the patch keys) and the attention over them
         topk = max(1, cfg.n_patch // 100)
         ws_probe = bsga.workspace(shape, bsga.OP_PROBE_SELECT, dev)
@@ -338,6 +362,9 @@ def main():
                          "flop_per_entry": BWD_FLOP_PER_ENTRY,
                          "TFLOP/s": round(bwd_tflops, 1),
                          "frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4)},
+            "step_latency_median_ms": {"warm": round(warm_median, 4),
+                                       "flushed_512MB": round(flushed_median, 4),
+                                       "steps": lat_reps},
             "dense_ms": round(dense_ms, 4),
             "speedup_vs_dense": round(dense_ms / ms, 3),
             "bsga_layer_call_ms": round(layer_call_ms, 4),
