@@ -6,11 +6,12 @@ Workload: the VGGT-shaped global layer at 32 frames of 518x518 (37x37 patches
 b = 128, rho = 0.75, tau = 0.9, with the planted-correspondence generator and
 10 % sink keys (synthetic; inputs resident in HBM before timing).
 
-One step = the whole hot path through the C ABI on one stream:
-bsga_predict_mask -> bsga_select -> bsga_pack_kv -> bsga_patch_rows_packed ->
-bsga_special_rows_packed (the kernels bsga_layer runs).  HIP events around the
-patch-row launch (block-sparse attention over the kept blocks plus the special
-keys) give that kernel's average duration.
+One step = the whole hot path through the C ABI (the kernels bsga_layer
+runs), on two streams: bsga_predict_mask -> bsga_select on the launch stream,
+bsga_pack_kv -> bsga_special_rows_packed beside them on a side stream, then
+bsga_patch_rows_packed once the mask and the packed K/V are ready.  HIP events
+around the patch-row launch (block-sparse attention over the kept blocks plus
+the special keys), on its stream, give that kernel's average duration.
 
 Prints ONE JSON line.  `value` is the layer's effective TFLOP/s:
 4 * 64 * (computed score entries) / layer time, counting kept patch-patch
@@ -181,31 +182,55 @@ def main():
     kv = torch.empty(bsga.packed_kv_bytes(shape) + 256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    stages = ("predict_mask", "select", "pack_kv", "patch_rows", "special_rows")
+    side = torch.cuda.Stream(device=dev)  # default priority, like every stream here
+    stages = ("predict_mask", "select", "pack_kv", "special_rows", "patch_rows")
+    on_side = ("pack_kv", "special_rows")
+    fork_ev, packed_ev, side_ev = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
 
     def step(rho, tau, ev=None):
-        mark = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
-        mark(0)
+        """One layer.  The mask (predict_mask, select) is built on the launch
+        stream while a side stream packs K/V and computes the special rows,
+        which need only Q and the packed K/V; the patch rows wait for both
+        the mask and the packed K/V, and the step ends when both streams are
+        done.  ev: per stage a (start, end) pair of timing events, recorded on
+        the stream the stage runs on."""
+        def rec(name, i):
+            if ev is not None:
+                ev[name][i].record(side if name in on_side else stream)
+        fork_ev.record(stream)
+        side.wait_event(fork_ev)
+        with torch.cuda.stream(side):
+            rec("pack_kv", 0)
+            bsga.pack_kv(shape, k, v, kv=kv)
+            rec("pack_kv", 1)
+            packed_ev.record(side)
+            rec("special_rows", 0)
+            bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
+            rec("special_rows", 1)
+            side_ev.record(side)
+        rec("predict_mask", 0)
         bsga.predict_mask(shape, q, k, probs=probs, ws=ws_pred)
-        mark(1)
+        rec("predict_mask", 1)
+        rec("select", 0)
         bsga.select(shape, probs, rho, tau, x.rho_per_head, row_ptr=row_ptr, col_idx=col_idx,
                     ws=ws_sel)
-        mark(2)
-        bsga.pack_kv(shape, k, v, kv=kv)
-        mark(3)
+        rec("select", 1)
+        stream.wait_event(packed_ev)
+        rec("patch_rows", 0)
         bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
-        mark(4)
-        bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
-        mark(5)
+        rec("patch_rows", 1)
+        stream.wait_event(side_ev)
 
     def timed(fn, steps, warmup, with_stage_events=False):
         """Average ms per step over `steps` timed steps, plus (optionally) the
-        average ms of each stage from HIP events recorded on the launch stream."""
+        average ms of each stage from HIP events recorded on the stream the
+        stage was launched on."""
         for _ in range(warmup):
             fn(None)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-               for _ in range(steps)] if with_stage_events else [None] * steps
+        mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        evs = [{name: (mk(), mk()) for name in stages} for _ in range(steps)] \
+            if with_stage_events else [None] * steps
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
@@ -216,8 +241,8 @@ def main():
         total = start.elapsed_time(stop) / steps
         per = None
         if with_stage_events:
-            per = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
-                   for j, name in enumerate(stages)}
+            per = {name: sum(e[name][0].elapsed_time(e[name][1]) for e in evs) / steps
+                   for name in stages}
         return total, per
 
     def timed_marks(fn, steps, warmup, marks):
@@ -263,6 +288,15 @@ def main():
         layer_call_ms, _ = timed(lambda _ev: bsga.layer(shape, q, k, v, cfg.rho, cfg.tau,
                                                         x.rho_per_head, bufs=bufs),
                                  args.steps, 2)
+        # the two-stream step must reproduce bsga_layer (one stream) byte for byte
+        step(cfg.rho, cfg.tau)
+        torch.cuda.synchronize()
+        same_as_layer = bool(torch.equal(o.view(torch.int16), bufs.o.view(torch.int16))
+                             and torch.equal(lse, bufs.lse)
+                             and torch.equal(row_ptr, bufs.row_ptr))
+        if not same_as_layer:
+            print("# WARNING: two-stream step differs from bsga_layer", file=sys.stderr,
+                  flush=True)
         ms0, st0 = timed(lambda ev: step(cfg.rho, 0.0, ev), max(3, args.steps // 2), 2, True)
         kern0 = st0["patch_rows"]
         rp0 = row_ptr.cpu().numpy()
@@ -368,6 +402,7 @@ def main():
             "dense_ms": round(dense_ms, 4),
             "speedup_vs_dense": round(dense_ms / ms, 3),
             "bsga_layer_call_ms": round(layer_call_ms, 4),
+            "step_equals_bsga_layer": same_as_layer,
             "diag_tau0": {"note": "diagnostic, not a config: tau=0 so the top-k budget binds",
                           "ms": round(ms0, 4),
                           "density": round((pp0 + sp0) / (cfg.heads * n * n), 4),
