@@ -354,7 +354,9 @@ def nmse(o_full: np.ndarray, o_sparse: np.ndarray) -> float:
 # ----------------------------------------------------------------------------
 def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_o: np.ndarray,
                             frames: int, patches_per_frame: int, special_per_frame: int,
-                            block: int, kept: Optional[List[np.ndarray]]):
+                            block: int, kept: Optional[List[np.ndarray]],
+                            query_blocks: Optional[Sequence[int]] = None,
+                            special_queries=True):
     """Gradients (dQ, dK, dV) of L = sum(O * dO) for one head, where O is the
     layer's output (patch queries over their kept patch blocks and every
     special key, special queries over every key; kept = None: dense).
@@ -363,7 +365,14 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_o: np
     P_t = softmax(l)_t and O = sum_t P_t v_t:
       dV_t += P_t dO,  dP_t = dO . v_t,  D = dO . O,  dS_t = P_t (dP_t - D),
       dQ = sum_t dS_t k_t / sqrt(d),  dK_t += dS_t q / sqrt(d).
-    Computed one query block (and the special queries) at a time."""
+    Computed one query block (and the special queries) at a time.
+
+    query_blocks / special_queries restrict the loss to some queries: only
+    the listed patch query blocks (all if None) and the special queries
+    (all if True, none if False, else the listed special tokens) contribute.
+    The dQ rows of those queries are then the full gradient; dK and dV hold
+    only their contributions (the full dK, dV are the sums over a partition
+    of the queries)."""
     spec, patch = token_roles(frames, patches_per_frame, special_per_frame)
     n = patch.shape[0]
     B = num_blocks(n, block)
@@ -371,15 +380,22 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, d_o: np
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     all_tok = np.arange(q.shape[0])
     groups = []
-    for i in range(B):
+    for i in (range(B) if query_blocks is None else query_blocks):
         qt = patch[block_members(n, block, i)]
         if kept is None:
             keys = all_tok
         else:
             keys = np.concatenate([patch_block_tokens(patch, block, kept[i]), spec])
         groups.append((qt, keys))
-    if spec.shape[0]:
-        groups.append((spec, all_tok))
+    if special_queries is True:
+        sq = spec
+    elif special_queries is False:
+        sq = spec[:0]
+    else:
+        sq = np.asarray(special_queries, dtype=np.int64)
+        assert np.all(np.isin(sq, spec)), "special_queries must be special tokens"
+    if sq.shape[0]:
+        groups.append((sq, all_tok))
     for qt, keys in groups:
         if keys.shape[0] == 0:
             continue

@@ -555,4 +555,45 @@ def pin_backward_closed_forms(O):
     assert np.allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
 
 
+def pin_backward_query_subsets(O):
+    """Restricted to some queries, the gradients are those of the loss over
+    those output rows only (central differences of the oracle's forward), and
+    the restricted calls over a partition of the queries add up to the full
+    gradients."""
+    (F, P, S, b), q, k, v, do, kept = _tiny_backward_case(2)
+    spec, _ = O.token_roles(F, P, S)
+    B = (F * P + b - 1) // b
+    part = O.attention_backward_head(q, k, v, do, F, P, S, b, kept, query_blocks=[1],
+                                     special_queries=[int(spec[-1])])
+    rows = set(O.layer_head(q, k, v, F, P, S, b, kept, query_blocks=[1],
+                            special_queries=False)) | {int(spec[-1])}
+
+    def loss(q_, k_, v_):
+        out = O.layer_head(q_, k_, v_, F, P, S, b, kept)
+        return sum(float(np.dot(out[t][0], do[t])) for t in out if t in rows)
+    h = 1e-6
+    for name, x, g in (("q", q, part[0]), ("k", k, part[1]), ("v", v, part[2])):
+        for idx in list(np.ndindex(x.shape))[::2]:
+            args = {"q_": q, "k_": k, "v_": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name + "_"] = xp
+            lp = loss(**args)
+            args[name + "_"] = xm
+            lm = loss(**args)
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 1e-7, (name, idx)
+    full = O.attention_backward_head(q, k, v, do, F, P, S, b, kept)
+    acc = [np.zeros_like(q) for _ in range(3)]
+    for i in range(B):
+        for a, g in zip(acc, O.attention_backward_head(q, k, v, do, F, P, S, b, kept,
+                                                       query_blocks=[i], special_queries=False)):
+            a += g
+    for a, g in zip(acc, O.attention_backward_head(q, k, v, do, F, P, S, b, kept,
+                                                   query_blocks=[], special_queries=True)):
+        a += g
+    for a, g in zip(acc, full):
+        assert np.allclose(a, g, atol=1e-13, rtol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
