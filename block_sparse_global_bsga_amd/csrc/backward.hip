@@ -23,6 +23,8 @@
 //   and V rows in registers; per query tile S = Q K^T and dP = dO V^T (Q, dO
 //   rows from LDS, row permutation pi), then dV^T += dO^T P and
 //   dK^T += Q^T dS from the accumulators.
+#include <type_traits>
+
 #include "bsga_internal.hpp"
 #include "tile_common.hpp"
 
@@ -310,48 +312,55 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const u32x4* vt = kt + KCH;
       const u32x4* ktt = kt + 2 * KCH;
       const int valid = tile_valid(tile_kp0(n, raw_cur));
+      // only a partial tile (the last patch block, the last special tile)
+      // masks keys past its end; full tiles run the same code without it
+      auto tile = [&](auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int R = 32 * t + pi_row(l32);
-        f32x16 s = {}, dp = {};
+        for (int t = 0; t < NS; ++t) {
+          const int R = 32 * t + pi_row(l32);
+          f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt[c]), qop[m], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vt[c]), dop[m], dp, 0, 0, 0);
-        }
-        if (!second) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-            const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
-            d_lane = fmaf(key < valid ? p : 0.f, dp[r], d_lane);
+          for (int m = 0; m < 4; ++m) {
+            const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt[c]), qop[m], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vt[c]), dop[m], dp, 0, 0, 0);
           }
-          continue;
-        }
+          if (!second) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          f32x8 e8, rem;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * h2 + e;
-            const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
-            const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-            e8[e] = key < valid ? p * (dp[r] - dq_d) : 0.f;
+            for (int r = 0; r < 16; ++r) {
+              const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+              const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
+              d_lane = fmaf((kFull || key < valid) ? p : 0.f, dp[r], d_lane);
+            }
+            continue;
           }
-          const bf16x8 ds_hi = __builtin_convertvector(e8, bf16x8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)ds_hi[e];
-          const bf16x8 ds_lo = __builtin_convertvector(rem, bf16x8);
-          const int ch = 4 * t + 2 * h2 + hh;
-          const bf16x8 k0 = as_bf16x8(ktt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
-          const bf16x8 k1 = as_bf16x8(ktt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
-          g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_hi, g0, 0, 0, 0);
-          g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_hi, g1, 0, 0, 0);
-          g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
-          g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_lo, g1, 0, 0, 0);
+          for (int h2 = 0; h2 < 2; ++h2) {
+            f32x8 e8, rem;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * h2 + e;
+              const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
+              const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
+              e8[e] = (kFull || key < valid) ? p * (dp[r] - dq_d) : 0.f;
+            }
+            const bf16x8 ds_hi = __builtin_convertvector(e8, bf16x8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)ds_hi[e];
+            const bf16x8 ds_lo = __builtin_convertvector(rem, bf16x8);
+            const int ch = 4 * t + 2 * h2 + hh;
+            const bf16x8 k0 = as_bf16x8(ktt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
+            const bf16x8 k1 = as_bf16x8(ktt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+            g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_hi, g0, 0, 0, 0);
+            g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_hi, g1, 0, 0, 0);
+            g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
+            g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_lo, g1, 0, 0, 0);
+          }
         }
-      }
+      };
+      if (valid == KT) tile(std::true_type{});
+      else tile(std::false_type{});
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       raw_cur = raw_nxt;
