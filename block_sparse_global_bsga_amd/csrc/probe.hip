@@ -105,8 +105,9 @@ __global__ __launch_bounds__(kTopkThreads) void probe_topk_kernel(const float* _
                                                                   int32_t* __restrict__ list,
                                                                   int32_t* __restrict__ count) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t bin_tot[4];
   __shared__ uint64_t s_prefix;
-  __shared__ int s_rem;
+  __shared__ int s_rem, s_done;
   __shared__ uint8_t keep[BSGA_MAX_BLOCKS];
   __shared__ int wave_tot[kTopkThreads / 64];
   const int h = blockIdx.x, T = threadIdx.x;
@@ -116,11 +117,15 @@ __global__ __launch_bounds__(kTopkThreads) void probe_topk_kernel(const float* _
   if (T == 0) {
     s_prefix = 0;
     s_rem = K;
+    s_done = 0;
   }
   __syncthreads();
   if (K > 0) {
     // MSB-first radix select, 8 bits per pass: after pass d the top 8(d+1)
-    // bits of the K-th largest key are known
+    // bits of the K-th largest key are known.  When the K-th largest falls in
+    // a bin that must be taken whole (every key with that prefix is among the
+    // top K), the prefix itself is the threshold and the select stops early;
+    // without ties in the scores that happens after the 4 score-bit passes.
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
@@ -132,20 +137,33 @@ __global__ __launch_bounds__(kTopkThreads) void probe_topk_kernel(const float* _
         if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1u);
       }
       __syncthreads();
-      if (T == 0) {
-        int rem = s_rem;
-        for (int bin = 255; bin >= 0; --bin) {
-          const int c = (int)hist[bin];
-          if (rem > c) {
-            rem -= c;
-          } else {
-            s_prefix = prefix | ((uint64_t)bin << shift);
-            break;
-          }
+      // thread T < 256 takes bin 255 - T: an inclusive scan over T counts the
+      // keys in that bin and every higher one
+      const int rem = s_rem;
+      uint32_t own = 0, incl = 0;
+      if (T < 256) {
+        own = hist[255 - T];
+        incl = own;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_up(incl, off);
+          if ((T & 63) >= off) incl += o;
         }
-        s_rem = rem;
+        if ((T & 63) == 63) bin_tot[T >> 6] = incl;
       }
       __syncthreads();
+      if (T < 256) {
+        for (int u = 0; u < (T >> 6); ++u) incl += bin_tot[u];
+        // the bin where the running count first reaches rem
+        if (incl >= (uint32_t)rem && incl - own < (uint32_t)rem) {
+          const uint32_t left = (uint32_t)rem - (incl - own);
+          s_prefix = prefix | ((uint64_t)(255 - T) << shift);
+          s_rem = (int)left;
+          s_done = left == own;
+        }
+      }
+      __syncthreads();
+      if (s_done) break;
     }
     const uint64_t thr = s_prefix;  // the K-th largest key
     for (int p = T; p < d.np; p += kTopkThreads)
