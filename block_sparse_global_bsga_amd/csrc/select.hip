@@ -106,6 +106,119 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(
   }
 }
 
+// The same selection with one wave per row, for rows of at most 512 blocks
+// (up to 65,536 patch tokens at b = 128): the row's keys, padded to 512 with
+// zeros (below every real key), stay in registers.  Sorted position
+// i = 8 * lane + r lives in register r of the lane, so the bitonic network's
+// partners i ^ j are registers of the same lane for j < 8 and the same
+// register of lane ^ (j / 8) for j >= 8 (a cross-lane exchange): no LDS and no
+// barriers.  The float64 prefix sums use a wave scan; the exactness argument
+// above makes the decision independent of that association.
+constexpr int kWaveRowKeys = 8;
+constexpr int kWaveRowMax = 64 * kWaveRowKeys;
+
+__device__ inline uint64_t xor_lanes(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__global__ __launch_bounds__(256) void select_rows_wave_kernel(
+    const float* __restrict__ probs, int B, int rows, SelectParams sp,
+    int32_t* __restrict__ counts, uint64_t* __restrict__ thresh) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // uniform per wave
+  const int h = row / B;
+  const float* p = probs + (size_t)row * B;
+  uint64_t key[kWaveRowKeys];
+#pragma unroll
+  for (int r = 0; r < kWaveRowKeys; ++r) {
+    const int j = kWaveRowKeys * lane + r;
+    key[r] = j < B ? rank_key(p[j], j) : 0ull;
+  }
+  // bitonic sort, descending: position i keeps the larger of the pair
+  // (i, i ^ j) iff (i & j) == 0 equals (i & k) == 0
+#pragma unroll
+  for (int k = 2; k <= kWaveRowMax; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < kWaveRowKeys) {
+#pragma unroll
+        for (int r = 0; r < kWaveRowKeys; ++r) {
+          if (r & j) continue;
+          const int i = kWaveRowKeys * lane + r;
+          const bool desc = (i & k) == 0;
+          const uint64_t a = key[r], b = key[r | j];
+          const bool a_big = a > b;
+          key[r] = (a_big == desc) ? a : b;
+          key[r | j] = (a_big == desc) ? b : a;
+        }
+      } else {
+        const int m = j / kWaveRowKeys;
+        const bool lo = (lane & m) == 0;
+        const bool desc = ((kWaveRowKeys * lane) & k) == 0;
+#pragma unroll
+        for (int r = 0; r < kWaveRowKeys; ++r) {
+          const uint64_t other = xor_lanes(key[r], m);
+          const bool keep_max = lo == desc;
+          const bool mine_big = key[r] > other;
+          key[r] = (mine_big == keep_max) ? key[r] : other;
+        }
+      }
+    }
+  }
+
+  const double tau = sp.tau;
+  int n_tau;
+  if (tau <= 0.0) {
+    n_tau = 0;
+  } else if (tau >= 1.0) {
+    n_tau = B;
+  } else {
+    double v[kWaveRowKeys], local = 0.0;
+#pragma unroll
+    for (int r = 0; r < kWaveRowKeys; ++r) {
+      v[r] = (double)__uint_as_float((uint32_t)(key[r] >> 32));
+      local += v[r];
+    }
+    double incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    double c_n = incl - local;  // exact: every partial sum here is exact
+    int found = kWaveRowMax + 1;
+#pragma unroll
+    for (int r = 0; r < kWaveRowKeys; ++r) {
+      c_n += v[r];
+      if (found > kWaveRowMax && c_n >= tau) found = kWaveRowKeys * lane + r + 1;
+    }
+    // the running sums grow with the position, so the first lane that
+    // reached tau holds the smallest such n
+    const uint64_t hit = __ballot(found <= kWaveRowMax);
+    n_tau = hit ? __shfl(found, __ffsll((unsigned long long)hit) - 1) : B;
+    n_tau = min(n_tau, B);
+  }
+  const int count = min(B, max(sp.k[h], n_tau));
+  uint64_t t = ~0ull;
+  if (count > 0) {
+    const int pos = count - 1, src = pos / kWaveRowKeys, reg = pos % kWaveRowKeys;
+    uint64_t mine = key[0];
+#pragma unroll
+    for (int r = 1; r < kWaveRowKeys; ++r)
+      if (reg == r) mine = key[r];
+    const uint32_t lo32 = (uint32_t)__shfl((int)(uint32_t)mine, src);
+    const uint32_t hi32 = (uint32_t)__shfl((int)(uint32_t)(mine >> 32), src);
+    t = ((uint64_t)hi32 << 32) | lo32;
+  }
+  if (lane == 0) {
+    counts[row] = count;
+    thresh[row] = t;
+  }
+}
+
 // Exclusive scan of the per-row counts into row_ptr (one workgroup).
 __global__ __launch_bounds__(1024) void scan_counts_kernel(const int32_t* __restrict__ counts,
                                                            int rows,
@@ -176,9 +289,14 @@ hipError_t launch_select(const Dims& d, const float* probs, const SelectParams& 
   int32_t* counts = (int32_t*)ws;
   uint64_t* thresh =
       (uint64_t*)((char*)ws + ((((size_t)rows * sizeof(int32_t)) + 255) & ~(size_t)255));
-  const int n_pad = pow2_at_least(d.B);
-  select_rows_kernel<<<rows, kSelThreads, n_pad * sizeof(uint64_t), st>>>(
-      probs, d.B, n_pad, sp, counts, thresh);
+  if (d.B <= kWaveRowMax) {
+    select_rows_wave_kernel<<<(rows + 3) / 4, 256, 0, st>>>(probs, d.B, rows, sp, counts,
+                                                             thresh);
+  } else {
+    const int n_pad = pow2_at_least(d.B);
+    select_rows_kernel<<<rows, kSelThreads, n_pad * sizeof(uint64_t), st>>>(
+        probs, d.B, n_pad, sp, counts, thresh);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   scan_counts_kernel<<<1, 1024, 0, st>>>(counts, rows, row_ptr);
