@@ -69,6 +69,8 @@ def compare_rows(out: dict, o_gpu: np.ndarray, lse_gpu: np.ndarray, roundings: i
     excess = diff - roundings * BF16_HALF_ULP * np.abs(o_ref)
     l_g = lse_gpu[toks].astype(np.float64)
     both_inf = np.isneginf(l_ref) & np.isneginf(l_g)
-    l_err = np.where(both_inf, 0.0, np.abs(l_g - l_ref))
+    l_err = np.zeros_like(l_ref)
+    np.subtract(l_g, l_ref, out=l_err, where=~both_inf)
+    l_err = np.abs(l_err)
     return (float(max(excess.max(), 0.0)), float(l_err.max()), float(np.mean(o_ref ** 2)),
             len(toks), float(diff.max()))

@@ -1,0 +1,134 @@
+"""Seeded sweep over random small layer shapes, each checked against the
+oracle end to end: frames 1-8, patch grids 2x2 to 32x32, 0-7 special tokens
+per frame, 1-3 heads, b = 64 or 128, head kinds diffuse / planted
+correspondences / position code, rho and tau drawn per shape (including
+tau = 0 and tau = 1), plus two shapes whose rows are all empty.
+
+Per shape, through the C ABI:
+* bsga_layer's CSR equals the oracle's selection of the GPU's own float32
+  probabilities, bit for bit, and those probabilities are within 1e-5 of
+  the oracle's (near-float32 pooled scores);
+* every output row: max |O_gpu - O_oracle| <= 2e-2 rms(O_dense) once the bf16
+  output rounding (half an ulp of |O|) is set aside, |dLSE| <= 2e-3 (rows
+  with no key at all: O = 0 and LSE = -inf on both sides);
+* bsga_attn_backward on a seeded dO: every gradient tensor of every head
+  within 2e-2 rms of the oracle's float64 gradients for the same mask, the
+  rms floored at 1e-3 of the element scale of the gradient's terms
+  (|dO| |v| |k| / 8 per row for dQ, |dO| |v| |q| / 8 for dK, |dO| for dV,
+  divided by 8 for one of the 64 elements).  Without the floor a head whose
+  softmax rows are one-hot to float64 precision (a planted correspondence
+  with itself as the only match) has dQ and dK near 1e-30, and float32
+  rounding of dS = P (dP - D), far below the terms' size, would count as
+  error; the floor is still 2^-15 of that size, above the hi + lo
+  arithmetic's rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from block_sparse_global_bsga_amd import synth
+from oracle import bsga_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2
+LSE_TOL = 2e-3
+P_TOL = 1e-5
+G_TOL = 2e-2
+
+
+def _shapes(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        frames = int(rng.integers(1, 9))
+        gh, gw = (int(x) for x in rng.integers(2, 33, size=2))
+        specials = int(rng.integers(0, 8))
+        heads = int(rng.integers(1, 4))
+        block = int(rng.choice([64, 128]))
+        kind = str(rng.choice(["diffuse", "corr", "pos"]))
+        rho = float(np.round(rng.uniform(0.0, 0.99), 2))
+        tau = float(rng.choice([0.0, 1.0, float(np.round(rng.uniform(0.3, 0.99), 2))]))
+        out.append((i, frames, gh, gw, specials, heads, block, kind, rho, tau))
+    # every row empty (k = 0, tau = 0): without special tokens no query of a
+    # patch has any key; with them, only the special keys remain
+    out.append((n, 3, 17, 9, 0, 2, 64, "corr", 0.99, 0.0))
+    out.append((n + 1, 3, 17, 9, 5, 2, 64, "corr", 0.99, 0.0))
+    return out
+
+
+SHAPES = _shapes()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_sparse_global_bsga_amd import bsga
+    return bsga
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"s{s[0]}-f{s[1]}-{s[2]}x{s[3]}-S{s[4]}"
+                         f"-h{s[5]}-b{s[6]}-{s[7]}-rho{s[8]}-tau{s[9]}")
+def test_random_shape(lib, shape):
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, head_f64, layer_shape, say, to_dev
+    i, frames, gh, gw, specials, heads, block, kind, rho, tau = shape
+    x = synth.random_layer(frames, gh, gw, heads, block, seed=500 + i,
+                           special_per_frame=specials, kind=kind, rho=rho, tau=tau)
+    cfg = x.cfg
+    shp = layer_shape(cfg)
+    say(f"[random shape {i}] N={cfg.tokens} (N_p {cfg.n_patch}, N_s {cfg.n_special}) H={heads} "
+        f"b={block} {kind} rho={rho} tau={tau}")
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    bufs = lib.layer(shp, q, k, v, rho, tau)
+    rng = np.random.default_rng(900 + i)
+    do_bits = synth.fp32_to_bf16_bits(
+        rng.standard_normal((heads, cfg.tokens, 64), dtype=np.float32))
+    grads = lib.attn_backward(shp, q, k, v, bufs.o, bufs.lse, to_dev(do_bits), bufs.row_ptr,
+                              bufs.col_idx)
+    torch.cuda.synchronize()
+    B = lib.num_blocks(shp)
+    probs = bufs.probs.cpu().numpy()
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx.cpu().numpy()[:rp[-1]]
+    ref_rp, ref_ci = O.select_blocks(probs, tau, rho)
+    assert np.array_equal(rp, ref_rp) and np.array_equal(ci, ref_ci), "mask differs"
+    o, lse = from_dev_bf16(bufs.o), bufs.lse.cpu().numpy()
+    g_gpu = [g.cpu().numpy() for g in grads]
+    _, patch = O.token_roles(frames, gh * gw, specials)
+    worst_p = worst_o = worst_l = 0.0
+    worst_g = [0.0, 0.0, 0.0]
+    acc = cnt = 0.0
+    def row_norm(a):
+        return float(np.sqrt(np.mean(np.sum(a ** 2, axis=1))))
+
+    for h in range(heads):
+        qh, kh, vh = head_f64(x, h)
+        doh = synth.bf16_bits_to_f64(do_bits[h])
+        nq, nk, nv, nd = row_norm(qh), row_norm(kh), row_norm(vh), row_norm(doh)
+        elem_scale = [nd * nv * nk / 8 / 8, nd * nv * nq / 8 / 8, nd / 8]
+        p_ref = O.predict_head(qh[patch], kh[patch], block)[3]
+        worst_p = max(worst_p, float(np.abs(probs[h] - p_ref).max()))
+        kept = O.kept_lists(rp, ci, h, B)
+        out = O.layer_head(qh, kh, vh, frames, gh * gw, specials, block, kept)
+        dense, _ = O.softmax_attention(qh, kh, vh)
+        acc += float(np.sum(dense ** 2))
+        cnt += dense.size
+        eo, el, _, _, _ = compare_rows(out, o[h], lse[h])
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        ref = O.attention_backward_head(qh, kh, vh, doh, frames, gh * gw, specials, block, kept)
+        for j in range(3):
+            rms = float(np.sqrt(np.mean(ref[j] ** 2)))
+            err = float(np.abs(g_gpu[j][h] - ref[j]).max())
+            worst_g[j] = max(worst_g[j], err / max(rms, 1e-3 * elem_scale[j], 1e-300))
+            if rms < 1e-3 * elem_scale[j]:
+                say(f"   head {h} grad {'QKV'[j]}: rms {rms:.1e} below 1e-3 of its term scale "
+                    f"{elem_scale[j]:.1e}; max err {err:.1e}")
+    rms_o = (acc / cnt) ** 0.5
+    say(f"   nnz {rp[-1]} of {heads * B * B}; |dP| {worst_p:.1e}; O err {worst_o / rms_o:.2e} rms; "
+        f"|dLSE| {worst_l:.1e}; grads dQ {worst_g[0]:.1e} dK {worst_g[1]:.1e} dV {worst_g[2]:.1e}")
+    assert worst_p <= P_TOL
+    assert worst_o <= O_TOL * rms_o and worst_l <= LSE_TOL
+    assert max(worst_g) <= G_TOL
