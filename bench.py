@@ -10,8 +10,10 @@ One step = the whole hot path through the C ABI (the kernels bsga_layer
 runs), on two streams: bsga_predict_mask -> bsga_select on the launch stream,
 bsga_pack_kv -> bsga_special_rows_packed beside them on a side stream, then
 bsga_patch_rows_packed once the mask and the packed K/V are ready.  HIP events
-around the patch-row launch (block-sparse attention over the kept blocks plus
-the special keys), on its stream, give that kernel's average duration.
+around that call (block-sparse attention over the kept blocks plus the
+special keys, with the rows of the last, partial round of workgroups split
+into key-range pieces, and the merge of those pieces), on its stream, give
+its average duration.
 
 Prints ONE JSON line.  `value` is the layer's effective TFLOP/s:
 4 * 64 * (computed score entries) / layer time, counting kept patch-patch
@@ -179,6 +181,7 @@ def main():
     ws_pred = bsga.workspace(shape, bsga.OP_PREDICT_MASK, dev)
     ws_sel = bsga.workspace(shape, bsga.OP_SELECT, dev)
     ws_spec = bsga.workspace(shape, bsga.OP_SPECIAL_DENSE_PACKED, dev)
+    ws_patch = bsga.workspace(shape, bsga.OP_PATCH_ROWS_PACKED, dev)
     kv = torch.empty(bsga.packed_kv_bytes(shape) + 256, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -217,7 +220,7 @@ def main():
         rec("select", 1)
         stream.wait_event(packed_ev)
         rec("patch_rows", 0)
-        bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
+        bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse, ws=ws_patch)
         rec("patch_rows", 1)
         stream.wait_event(side_ev)
 
@@ -338,7 +341,7 @@ def main():
             bsga.probe_select(shape, q, k, topk, row_ptr=row_ptr, col_idx=col_idx, ws=ws_probe)
             mark(1)
             bsga.pack_kv(shape, k, v, kv=kv)
-            bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse)
+            bsga.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o, lse, ws=ws_patch)
             bsga.special_rows_packed(shape, q, kv, o, lse, ws=ws_spec)
             mark(2)
 
@@ -456,7 +459,8 @@ def main():
         "layer_frac_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "density": round(density, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": "attn_kernel<128, 128, kSparseFused> (bsga_patch_rows_packed)",
+                     "kernel": "attn_kernel<128, 128, kSparseTail> + tail_merge_kernel "
+                               "(bsga_patch_rows_packed)",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic()},

@@ -27,7 +27,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 (OP_PREDICT_MASK, OP_SELECT, OP_SPARSE_ATTN, OP_SPECIAL_DENSE, OP_DENSE_ATTN, OP_LAYER,
- OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT, OP_NMSE, OP_BACKWARD) = range(10)
+ OP_SPECIAL_DENSE_PACKED, OP_PROBE_SELECT, OP_NMSE, OP_BACKWARD,
+ OP_PATCH_ROWS_PACKED) = range(11)
 MAX_HEADS = 256
 MAX_BLOCKS = 4096
 
@@ -76,7 +77,8 @@ _lib.bsga_sparse_attn_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _
 _lib.bsga_special_dense_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p,
                                            ctypes.c_size_t, _p]
 _lib.bsga_dense_attn_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p]
-_lib.bsga_patch_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p, _p, _p]
+_lib.bsga_patch_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p, _p, _p,
+                                        ctypes.c_size_t, _p]
 _lib.bsga_special_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, _p,
                                           ctypes.c_size_t, _p]
 _lib.bsga_layer.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p, _p,
@@ -392,11 +394,18 @@ def dense_attn_packed(shape: LayerShape, q, kv, o, lse):
     return o, lse
 
 
-def patch_rows_packed(shape: LayerShape, q, kv, row_ptr, col_idx, o, lse):
+def patch_rows_packed(shape: LayerShape, q, kv, row_ptr, col_idx, o, lse, *, ws="auto"):
+    """Final patch rows.  ws: a workspace of workspace_bytes(OP_PATCH_ROWS_PACKED)
+    (allocated here when "auto"), or None to compute every row in one
+    workgroup (no tail splitting)."""
     _bf16(q, "q", shape)
+    if isinstance(ws, str):
+        ws = workspace(shape, OP_PATCH_ROWS_PACKED, q.device)
     _check(_lib.bsga_patch_rows_packed(ctypes.byref(shape.c()), _ptr(q), _ws_ptr(kv), _ws_len(kv),
                                        _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse),
-                                       _stream(q.device)), "bsga_patch_rows_packed")
+                                       None if ws is None else _ws_ptr(ws),
+                                       0 if ws is None else _ws_len(ws), _stream(q.device)),
+           "bsga_patch_rows_packed")
     return o, lse
 
 

@@ -60,7 +60,18 @@ namespace bsga {
 // kSpecialSplit: special queries x a range of key tiles (split-K partials)
 // kPatchSpecial: patch queries x special tiles, merged by log-sum-exp into
 //                the patch rows already in O/LSE
-enum Mode { kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4 };
+// kSparseTail:   kSparseFused, except that the rows of each XCD's last,
+//                partial round of workgroups are split into kTailPieces pieces
+//                of consecutive key tiles, listed piece-major after the XCD's
+//                whole rows: the in-order dispatch then spreads that round
+//                over every slot, and concurrent pieces read the same key range
+//                of consecutive rows; tail_merge_kernel combines the pieces
+enum Mode {
+  kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5
+};
+
+// pieces per row of the last round (kSparseTail)
+constexpr int kTailPieces = 8;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -77,6 +88,8 @@ struct AttnArgs {
   int q_tiles;
   int nsplit;
   int tiles_per_split;
+  int rows_per_xcd;  // kSparseTail: rows of each XCD (as xcd_item)
+  int tail_m;        // kSparseTail: workgroup slots per XCD (one round)
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
@@ -102,53 +115,81 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   __shared__ u32x4 smem[4 * KCH];   // K slots 0, 1 then V^T slots 0, 1
 
   const Dims& d = a.d;
-  const int item = xcd_item(blockIdx.x, a.n_items);
-  if (item < 0) return;
   const int T = threadIdx.x, lane = T & 63;
   const int w = __builtin_amdgcn_readfirstlane(T >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
 
-  int h, qp0, nt, tile0 = 0, split = 0, nt_csr = 0;
+  // What the tile loop works on: head h, the query tile starting at packed
+  // row qp0, and its list of nt key tiles (a CSR row, then the special tiles;
+  // a range of tiles; or every tile).
+  int h = 0, qp0 = 0, nt = 0, tile0 = 0, split = 0, nt_csr = 0;
+  int piece = -1;         // kSparseTail: the piece of the row, or -1 (whole row)
+  size_t piece_slot = 0;  // kSparseTail: its partial's slot
   const int32_t* cols = nullptr;
-  if constexpr (MODE == kSparse || MODE == kSparseFused) {
-    h = item / d.B;
-    qp0 = (item - h * d.B) * QT;
-    const int r0 = a.row_ptr[item];
-    cols = a.col_idx + r0;
-    nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
-    nt = nt_csr * TPB + (MODE == kSparseFused ? d.ns_pad / KT : 0);
-  } else if constexpr (MODE == kDense) {
-    h = item / a.q_tiles;
-    qp0 = (item - h * a.q_tiles) * QT;
-    nt = d.ntot_pad / KT;
-  } else if constexpr (MODE == kSpecialSplit) {
-    const int per_h = a.q_tiles * a.nsplit;
-    h = item / per_h;
-    const int rem = item - h * per_h;
-    const int qt = rem / a.nsplit;
-    split = rem - qt * a.nsplit;
-    qp0 = d.np_pad + qt * QT;
-    tile0 = split * a.tiles_per_split;
-    nt = max(0, min(a.tiles_per_split, d.ntot_pad / KT - tile0));
-  } else {
-    h = item / a.q_tiles;
-    qp0 = (item - h * a.q_tiles) * QT;
-    tile0 = d.np_pad / KT;
-    nt = d.ns_pad / KT;
+  {
+    int item;
+    if constexpr (MODE == kSparseTail) {
+      const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+      const int r0 = x * a.rows_per_xcd;
+      const int n_x = min(a.n_items, r0 + a.rows_per_xcd) - r0;
+      if (n_x <= 0) return;
+      const int full = n_x / a.tail_m * a.tail_m, rem = n_x - full;
+      if (j < full) {
+        item = r0 + j;
+      } else {
+        const int q = j - full;
+        if (q >= rem * kTailPieces) return;
+        const int t = q % rem;
+        piece = q / rem;
+        item = r0 + full + t;
+        // every XCD before the last holds rows_per_xcd rows
+        piece_slot = ((size_t)x * (a.rows_per_xcd % a.tail_m) + t) * kTailPieces + piece;
+      }
+    } else {
+      item = xcd_item(blockIdx.x, a.n_items);
+      if (item < 0) return;
+    }
+    if constexpr (MODE == kSparse || MODE == kSparseFused || MODE == kSparseTail) {
+      h = item / d.B;
+      qp0 = (item - h * d.B) * QT;
+      const int r0 = a.row_ptr[item];
+      cols = a.col_idx + r0;
+      nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
+      nt = nt_csr * TPB + (MODE == kSparse ? 0 : d.ns_pad / KT);
+    } else if constexpr (MODE == kDense) {
+      h = item / a.q_tiles;
+      qp0 = (item - h * a.q_tiles) * QT;
+      nt = d.ntot_pad / KT;
+    } else if constexpr (MODE == kSpecialSplit) {
+      const int per_h = a.q_tiles * a.nsplit;
+      h = item / per_h;
+      const int rem = item - h * per_h;
+      const int qt = rem / a.nsplit;
+      split = rem - qt * a.nsplit;
+      qp0 = d.np_pad + qt * QT;
+      tile0 = split * a.tiles_per_split;
+      nt = max(0, min(a.tiles_per_split, d.ntot_pad / KT - tile0));
+    } else {
+      h = item / a.q_tiles;
+      qp0 = (item - h * a.q_tiles) * QT;
+      tile0 = d.np_pad / KT;
+      nt = d.ns_pad / KT;
+    }
+    // everything above is wave-uniform; keep it in scalar registers
+    h = __builtin_amdgcn_readfirstlane(h);
+    qp0 = __builtin_amdgcn_readfirstlane(qp0);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
+    tile0 = __builtin_amdgcn_readfirstlane(tile0);
   }
-  // everything above is wave-uniform; keep it in scalar registers
-  h = __builtin_amdgcn_readfirstlane(h);
-  qp0 = __builtin_amdgcn_readfirstlane(qp0);
-  nt = __builtin_amdgcn_readfirstlane(nt);
-  nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
-  tile0 = __builtin_amdgcn_readfirstlane(tile0);
   // Position of tile n, in two steps so that the global load of a CSR entry
   // can be issued long before its value is consumed: tile_raw(n) loads the
   // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
   // it into the tile's first packed key.  Kept block j of the row covers tiles
   // j TPB .. j TPB + TPB - 1.
+  constexpr bool kCsr = MODE == kSparse || MODE == kSparseFused || MODE == kSparseTail;
   auto tile_raw = [&](int n) -> int {
-    if constexpr (MODE == kSparse || MODE == kSparseFused) {
+    if constexpr (kCsr) {
       return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0;
     } else {
       return 0;
@@ -156,9 +197,9 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   };
   auto tile_kp0 = [&](int n, int raw) -> int {
     raw = __builtin_amdgcn_readfirstlane(raw);
-    if constexpr (MODE == kSparse || MODE == kSparseFused) {
+    if constexpr (kCsr) {
       const int nb = nt_csr * TPB;
-      if (MODE == kSparseFused && n >= nb) return d.np_pad + (n - nb) * KT;
+      if (MODE != kSparse && n >= nb) return d.np_pad + min(n - nb, d.ns_pad / KT - 1) * KT;
       return min(max(raw, 0), d.B - 1) * QT + (n % TPB) * KT;
     } else {
       return (tile0 + n) * KT;
@@ -168,30 +209,16 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
   };
 
-  // the wave's 32 query rows: lane half hh holds dims [32hh, 32hh + 32)
-  bf16x8 qop[4];
-  {
-    const int qtok = packed_token(qp0 + 32 * w + l32, d);
-    const u32x4* src =
-        (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      u32x4 t = u32x4{0, 0, 0, 0};
-      if (qtok >= 0) t = src[m];
-      qop[m] = as_bf16x8(t);
-    }
-  }
-
   // ---- direct-to-LDS tile loads into two rings (K rows, V^T rows), two
   // slots each.  Every wave issues LPW loads of 64 x 16 B per K tile and LPW
   // per V^T tile; load i of wave w fills chunks (LPW w + i) * 64 + lane.
   // The swizzle of the row a lane fills depends on i only through i mod 2
   // (K, and V^T of 64-key tiles) or i mod 4 (V^T of 128-key tiles), so a few
   // per-lane byte offsets cover all loads.  Addresses are a uniform base
-  // (scalar registers) plus a 32-bit per-lane offset.
-  const char* kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * kHeadDim * 2;
+  // (scalar registers, the head's) plus a 32-bit per-lane offset.
   const uint32_t vrow_bytes = (uint32_t)d.ntot_pad * 2;
-  const char* vbase = (const char*)a.vt + (size_t)h * kHeadDim * vrow_bytes;
+  const char* kbase = nullptr;
+  const char* vbase = nullptr;
   uint32_t koff[2], voff[4];
   {
     const int r0 = lane >> 3, pc = lane & 7;
@@ -234,6 +261,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   // tile, first tile, or its exact max more than 64 log2 units above the
   // running max) selects the rare block that masks, takes the exact max and
   // rescales O and l.
+  bf16x8 qop[4];  // the wave's 32 query rows: lane half hh holds dims [32hh, 32hh + 32)
   f32x16 o0 = {}, o1 = {};
   float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units (scores * log2(e)/8)
 
@@ -302,105 +330,149 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     return valid < KT || __any(!(mx * kScaleLog2 - m_run <= kLazySlack));
   };
 
+  // Tiles n0 .. n1 - 1 of the current segment, from a fresh softmax state.
   // CSR entries run two tiles ahead of the compute: the entry of tile n+2 is
   // loaded during iteration n and consumed after that iteration's closing
   // wait, so no wait in the middle of an iteration (which would also stall on
-  // the tile prefetch) is needed.
-  int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
-  if (nt > 0) {
-    const int kp0 = tile_kp0(0, raw_cur);
-    issue_k(kp0, 0);
-    issue_v(kp0, 0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  f32x16 s[NS];
-  for (int n = 0; n < nt; ++n) {
-    const int slot = n & 1;
-    if (n + 1 < nt) {
-      const int kp1 = tile_kp0(n + 1, raw_nxt);
-      issue_k(kp1, slot ^ 1);
-      issue_v(kp1, slot ^ 1);
+  // the tile prefetch) is needed.  The closing barrier of the last tile also
+  // frees both LDS rings for the next segment.
+  auto run_tiles = [&](int n0, int n1) {
+    {
+      const int qtok = packed_token(qp0 + 32 * w + l32, d);
+      const u32x4* src =
+          (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x4 t = u32x4{0, 0, 0, 0};
+        if (qtok >= 0) t = src[m];
+        qop[m] = as_bf16x8(t);
+      }
     }
-    const int raw_after = tile_raw(n + 2);
-    const u32x4* kt = smem + slot * KCH;
-    const u32x4* vt = smem + (2 + slot) * KCH;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) scores_t(s[t], mx, kt, t);
-    const int valid = tile_valid(tile_kp0(n, raw_cur));
-    if (n == 0 || needs_rare(mx, valid)) rare(s, mx, valid);
-    float ls = 0.f;
-    // the exponential / P V stretch runs at raised issue priority, so that a
-    // wave in it keeps the SIMD's other wave (typically in its score MFMAs)
-    // from starving the VALU
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int t = 0; t < NS; ++t) exp_pv_t(s[t], ls, vt, t);
-    __builtin_amdgcn_s_setprio(0);
-    l_run += ls;
+    kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * kHeadDim * 2;
+    vbase = (const char*)a.vt + (size_t)h * kHeadDim * vrow_bytes;
+    o0 = f32x16{};
+    o1 = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    int raw_cur = tile_raw(n0), raw_nxt = tile_raw(n0 + 1);
+    if (n1 > n0) {
+      const int kp0 = tile_kp0(n0, raw_cur);
+      issue_k(kp0, 0);
+      issue_v(kp0, 0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    raw_cur = raw_nxt;
-    raw_nxt = raw_after;
-  }
+    f32x16 s[NS];
+    for (int n = n0; n < n1; ++n) {
+      const int slot = (n - n0) & 1;
+      if (n + 1 < n1) {
+        const int kp1 = tile_kp0(n + 1, raw_nxt);
+        issue_k(kp1, slot ^ 1);
+        issue_v(kp1, slot ^ 1);
+      }
+      const int raw_after = tile_raw(n + 2);
+      const u32x4* kt = smem + slot * KCH;
+      const u32x4* vt = smem + (2 + slot) * KCH;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) scores_t(s[t], mx, kt, t);
+      const int valid = tile_valid(tile_kp0(n, raw_cur));
+      if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
+      float ls = 0.f;
+      // the exponential / P V stretch runs at raised issue priority, so that a
+      // wave in it keeps the SIMD's other wave (typically in its score MFMAs)
+      // from starving the VALU
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) exp_pv_t(s[t], ls, vt, t);
+      __builtin_amdgcn_s_setprio(0);
+      l_run += ls;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      raw_cur = raw_nxt;
+      raw_nxt = raw_after;
+    }
+  };
 
-  // o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32]
-  const float l_tot = xor32_sum(l_run);
-  const int qp = qp0 + 32 * w + l32;
-  if constexpr (MODE == kSpecialSplit) {
-    const int sq = qp - d.np_pad;
-    const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
-    float4* po = (float4*)(a.part_o + slot * kHeadDim);
+  // ---- epilogues.  o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32].
+  // Unnormalised float32 partial of the wave's 32 rows, with the running max
+  // (log2 units, or raw-score units if `raw`) and the row sum.
+  auto store_partial = [&](float* po_base, float* pml, bool raw) {
+    const float l_tot = xor32_sum(l_run);
+    float4* po = (float4*)po_base;
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       po[(8 * aa + 4 * hh) / 4] = make_float4(o0[4 * aa], o0[4 * aa + 1], o0[4 * aa + 2], o0[4 * aa + 3]);
       po[(32 + 8 * aa + 4 * hh) / 4] = make_float4(o1[4 * aa], o1[4 * aa + 1], o1[4 * aa + 2], o1[4 * aa + 3]);
     }
     if (hh == 0) {
-      a.part_ml[slot * 2] = m_run / kScaleLog2;  // raw-score units for the reduction
-      a.part_ml[slot * 2 + 1] = l_tot;
-    }
-    return;
-  }
-  const int qtok = packed_token(qp, d);
-  if (qtok < 0) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // natural-log LSE: (m_run + log2 l) ln 2
-  const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-  uint16_t* orow = a.o + ((size_t)h * d.n + qtok) * kHeadDim;
-  float* lrow = a.lse + (size_t)h * d.n + qtok;
-  float cp = 0.f, cs = inv, lse_out = lse;
-  if constexpr (MODE == kPatchSpecial) {
-    const float lse_p = *lrow;
-    const float M = fmaxf(lse_p, lse);
-    const float wp = lse_p == -INFINITY ? 0.f : expf(lse_p - M);
-    const float ws = lse == -INFINITY ? 0.f : expf(lse - M);
-    const float den = wp + ws;
-    cp = den > 0.f ? wp / den : 0.f;
-    cs = den > 0.f ? ws * inv / den : 0.f;
-    lse_out = den > 0.f ? M + logf(den) : -INFINITY;
-  }
-  auto store_half = [&](const f32x16 ou, int u) {
-#pragma unroll
-    for (int aa = 0; aa < 4; ++aa) {
-      u32x2* dst = (u32x2*)(orow + 32 * u + 8 * aa + 4 * hh);
-      f32x4 x;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = ou[4 * aa + c] * cs;
-      if constexpr (MODE == kPatchSpecial) {
-        const u32x2 old = *dst;
-        x[0] += cp * __uint_as_float(old[0] << 16);
-        x[1] += cp * __uint_as_float(old[0] & 0xffff0000u);
-        x[2] += cp * __uint_as_float(old[1] << 16);
-        x[3] += cp * __uint_as_float(old[1] & 0xffff0000u);
-      }
-      *dst = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+      pml[0] = raw ? m_run / kScaleLog2 : m_run;
+      pml[1] = l_tot;
     }
   };
-  store_half(o0, 0);
-  store_half(o1, 1);
-  if (hh == 0) *lrow = lse_out;
+  // final rows of O (bf16) and LSE; kPatchSpecial merges into the rows present
+  auto store_rows = [&]() {
+    const float l_tot = xor32_sum(l_run);
+    const int qtok = packed_token(qp0 + 32 * w + l32, d);
+    if (qtok < 0) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // natural-log LSE: (m_run + log2 l) ln 2
+    const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    uint16_t* orow = a.o + ((size_t)h * d.n + qtok) * kHeadDim;
+    float* lrow = a.lse + (size_t)h * d.n + qtok;
+    float cp = 0.f, cs = inv, lse_out = lse;
+    if constexpr (MODE == kPatchSpecial) {
+      const float lse_p = *lrow;
+      const float M = fmaxf(lse_p, lse);
+      const float wp = lse_p == -INFINITY ? 0.f : expf(lse_p - M);
+      const float ws = lse == -INFINITY ? 0.f : expf(lse - M);
+      const float den = wp + ws;
+      cp = den > 0.f ? wp / den : 0.f;
+      cs = den > 0.f ? ws * inv / den : 0.f;
+      lse_out = den > 0.f ? M + logf(den) : -INFINITY;
+    }
+    auto store_half = [&](const f32x16 ou, int u) {
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        u32x2* dst = (u32x2*)(orow + 32 * u + 8 * aa + 4 * hh);
+        f32x4 x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = ou[4 * aa + c] * cs;
+        if constexpr (MODE == kPatchSpecial) {
+          const u32x2 old = *dst;
+          x[0] += cp * __uint_as_float(old[0] << 16);
+          x[1] += cp * __uint_as_float(old[0] & 0xffff0000u);
+          x[2] += cp * __uint_as_float(old[1] << 16);
+          x[3] += cp * __uint_as_float(old[1] & 0xffff0000u);
+        }
+        *dst = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+      }
+    };
+    store_half(o0, 0);
+    store_half(o1, 1);
+    if (hh == 0) *lrow = lse_out;
+  };
+
+  if constexpr (MODE == kSparseTail) {
+    if (piece < 0) {
+      run_tiles(0, nt);
+      store_rows();
+    } else {
+      run_tiles(nt * piece / kTailPieces, nt * (piece + 1) / kTailPieces);
+      const size_t row = piece_slot * QT + 32 * w + l32;
+      store_partial(a.part_o + row * kHeadDim, a.part_ml + row * 2, false);
+    }
+  } else {
+    run_tiles(0, nt);
+    if constexpr (MODE == kSpecialSplit) {
+      const int sq = qp0 + 32 * w + l32 - d.np_pad;
+      const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
+      // raw-score units for the reduction
+      store_partial(a.part_o + slot * kHeadDim, a.part_ml + slot * 2, true);
+    } else {
+      store_rows();
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -430,6 +502,54 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
   o[((size_t)h * d.n + tok) * kHeadDim + lane] =
       __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
   if (lane == 0) lse[(size_t)h * d.n + tok] = M * 0.125f + logf(L);
+}
+
+// ---------------------------------------------------------------------------
+// Rows that kSparseTail split into pieces: workgroup (XCD x and tail row t,
+// group g of 4 query rows) merges the row's kTailPieces float32 partials by
+// log-sum-exp and writes O and LSE of those queries; thread T owns dimension
+// T % 64 of query 4 g + T / 64.  Many small workgroups keep the partials'
+// reads in flight (the merge is memory-bound).
+__global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml,
+                                                         uint16_t* __restrict__ o,
+                                                         float* __restrict__ lse, Dims d,
+                                                         int rows, int rows_per_xcd, int m) {
+  constexpr int QT = 128;
+  const int x = blockIdx.x / m, t = blockIdx.x % m;
+  const int r0 = x * rows_per_xcd;
+  const int n_x = min(rows, r0 + rows_per_xcd) - r0;
+  if (n_x <= 0) return;
+  const int full = n_x / m * m, rem = n_x - full;
+  if (t >= rem) return;
+  const int item = r0 + full + t;
+  const size_t slot0 = ((size_t)x * (rows_per_xcd % m) + t) * kTailPieces;
+  const int T = threadIdx.x, dim = T & 63, qr = 4 * blockIdx.y + (T >> 6);
+  float mi[kTailPieces], li[kTailPieces], oi[kTailPieces];
+  float M = -INFINITY;
+#pragma unroll
+  for (int pc = 0; pc < kTailPieces; ++pc) {
+    const size_t row = (slot0 + pc) * QT + qr;
+    mi[pc] = part_ml[row * 2];
+    li[pc] = part_ml[row * 2 + 1];
+    oi[pc] = part_o[row * kHeadDim + dim];
+    M = fmaxf(M, mi[pc]);
+  }
+  float acc = 0.f, l = 0.f;
+#pragma unroll
+  for (int pc = 0; pc < kTailPieces; ++pc) {
+    if (mi[pc] == -INFINITY) continue;  // an empty piece, or no key at all
+    const float wgt = fast_exp2(mi[pc] - M);
+    acc += oi[pc] * wgt;
+    l += li[pc] * wgt;
+  }
+  const int h = item / d.B;
+  const int tok = packed_token((item - h * d.B) * QT + qr, d);
+  if (tok < 0) return;
+  o[((size_t)h * d.n + tok) * kHeadDim + dim] =
+      __builtin_bit_cast(uint16_t, (__bf16)(l > 0.f ? acc / l : 0.f));
+  if (dim == 0)
+    lse[(size_t)h * d.n + tok] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -512,13 +632,66 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   return d.b == 64 ? run_attn<64, 64, kSparse>(a, st) : run_attn<128, 128, kSparse>(a, st);
 }
 
+// kSparseTail plan: slots per XCD (two 128 x 128 workgroups per compute unit;
+// 64 when the device cannot be queried) and the compact slot count of the
+// pieces of every XCD's last, partial round.
+struct TailPlan {
+  int m, rows, rows_per_xcd, slots, grid;
+};
+static TailPlan tail_plan(const Dims& d) {
+  TailPlan p;
+  int dev = 0, cus = 0;
+  p.m = 64;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus >= kXcds / 2)
+    p.m = 2 * cus / kXcds;
+  p.rows = d.H * d.B;
+  p.rows_per_xcd = (p.rows + kXcds - 1) / kXcds;
+  p.slots = 0;
+  p.grid = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
+    if (n_x <= 0) break;
+    const int full = n_x / p.m * p.m, rem = n_x - full;
+    p.slots = x * (p.rows_per_xcd % p.m) + rem;  // the last non-empty XCD's base + its rows
+    p.grid = max(p.grid, full + rem * kTailPieces);
+  }
+  p.slots *= kTailPieces;
+  return p;
+}
+static size_t tail_part_o_bytes(const TailPlan& p) {
+  return ((size_t)p.slots * 128 * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t patch_rows_workspace(const Dims& d) {
+  if (d.b != 128) return 0;
+  const TailPlan p = tail_plan(d);
+  return tail_part_o_bytes(p) + (size_t)p.slots * 128 * 2 * sizeof(float);
+}
+
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                              const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                             uint16_t* o, float* lse, hipStream_t st) {
+                             uint16_t* o, float* lse, hipStream_t st, void* ws, size_t ws_bytes) {
   AttnArgs a = base_args(d, q, kp, vt, o, lse);
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
+  if (d.b == 128 && ws != nullptr) {
+    const TailPlan p = tail_plan(d);
+    if (p.slots > 0 && ws_bytes >= tail_part_o_bytes(p) + (size_t)p.slots * 128 * 2 * sizeof(float)) {
+      a.part_o = (float*)ws;
+      a.part_ml = (float*)((char*)ws + tail_part_o_bytes(p));
+      a.rows_per_xcd = p.rows_per_xcd;
+      a.tail_m = p.m;
+      attn_kernel<128, 128, kSparseTail, 2><<<kXcds * p.grid, 256, 0, st>>>(a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      tail_merge_kernel<<<dim3(kXcds * p.m, 128 / 4), 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d,
+                                                                     p.rows, p.rows_per_xcd, p.m);
+      return hipGetLastError();
+    }
+  }
   return d.b == 64 ? run_attn<64, 64, kSparseFused>(a, st) : run_attn<128, 128, kSparseFused>(a, st);
 }
 

@@ -79,6 +79,7 @@ size_t ws_special(const Dims& d) { return up(special_workspace(d)); }
 size_t ws_probe(const Dims& d) { return up(probe_workspace(d)); }
 size_t ws_nmse(const Dims& d) { return up(nmse_workspace(d)); }
 size_t ws_backward(const Dims& d) { return up(backward_workspace(d)); }
+size_t ws_patch_rows(const Dims& d) { return up(patch_rows_workspace(d)); }
 
 size_t ws_for(const Dims& d, int op) {
   switch (op) {
@@ -91,10 +92,12 @@ size_t ws_for(const Dims& d, int op) {
     case BSGA_OP_PROBE_SELECT: return ws_probe(d);
     case BSGA_OP_NMSE: return ws_nmse(d);
     case BSGA_OP_BACKWARD: return ws_backward(d);
+    case BSGA_OP_PATCH_ROWS_PACKED: return ws_patch_rows(d);
     case BSGA_OP_LAYER: {
       size_t m = ws_predict(d);
       if (ws_select(d) > m) m = ws_select(d);
       if (ws_special(d) > m) m = ws_special(d);
+      if (ws_patch_rows(d) > m) m = ws_patch_rows(d);
       return ws_pack(d) + m;
     }
     default: return 0;
@@ -193,7 +196,7 @@ int bsga_csr_capacity(const bsga_shape* shape, int64_t* entries) {
 
 int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes) {
   BSGA_TRY(check_shape(shape));
-  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_BACKWARD)
+  if (!bytes || op < BSGA_OP_PREDICT_MASK || op > BSGA_OP_PATCH_ROWS_PACKED)
     return BSGA_ERR_INVALID_ARG;
   *bytes = ws_for(make_dims(*shape), op);
   return BSGA_OK;
@@ -394,7 +397,7 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q, const voi
 
 int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q, const void* kv,
                            size_t kv_bytes, const int32_t* row_ptr, const int32_t* col_idx,
-                           uint16_t* o, float* lse, void* stream) {
+                           uint16_t* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   BSGA_TRY(check_shape(shape));
   const Dims d = make_dims(*shape);
   BSGA_TRY(check_ptr(q, 16));
@@ -403,9 +406,11 @@ int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q, const voi
   BSGA_TRY(check_ptr(col_idx, 4));
   BSGA_TRY(check_ptr(o, 16));
   BSGA_TRY(check_ptr(lse, 4));
+  if (ws != nullptr) BSGA_TRY(check_ws(d, BSGA_OP_PATCH_ROWS_PACKED, ws, ws_bytes));
   const uint16_t* kp = (const uint16_t*)kv;
   return hip_status(launch_patch_rows(d, q, kp, kp + (size_t)d.H * d.ntot_pad * kHeadDim,
-                                      row_ptr, col_idx, o, lse, (hipStream_t)stream));
+                                      row_ptr, col_idx, o, lse, (hipStream_t)stream, ws,
+                                      ws ? ws_bytes : 0));
 }
 
 int bsga_special_rows_packed(const bsga_shape* shape, const uint16_t* q, const void* kv,
@@ -450,7 +455,8 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, co
   BSGA_TRY(hip_status(launch_softmax(d, probs, st)));
   BSGA_TRY(hip_status(launch_select(d, probs, sp, row_ptr, col_idx, scratch, st)));
   BSGA_TRY(hip_status(launch_pack(d, k, v, kp, vt, st)));
-  BSGA_TRY(hip_status(launch_patch_rows(d, q, kp, vt, row_ptr, col_idx, o, lse, st)));
+  BSGA_TRY(hip_status(launch_patch_rows(d, q, kp, vt, row_ptr, col_idx, o, lse, st, scratch,
+                                        ws_bytes - ws_pack(d))));
   return hip_status(launch_special_rows(d, q, kp, vt, o, lse, scratch, st));
 }
 

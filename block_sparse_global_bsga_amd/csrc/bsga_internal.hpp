@@ -140,9 +140,13 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q,
                               const uint16_t* kp, const uint16_t* vt,
                               const int32_t* row_ptr, const int32_t* col_idx,
                               uint16_t* o, float* lse, hipStream_t st);
+// ws (optional, patch_rows_workspace bytes): lets b = 128 rows of the last,
+// partial round of workgroups run as key-range pieces merged afterwards
+size_t patch_rows_workspace(const Dims& d);
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                              const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                             uint16_t* o, float* lse, hipStream_t st);
+                             uint16_t* o, float* lse, hipStream_t st, void* ws = nullptr,
+                             size_t ws_bytes = 0);
 size_t special_workspace(const Dims& d);
 hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                                const uint16_t* vt, uint16_t* o, float* lse, void* ws,

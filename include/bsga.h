@@ -71,7 +71,8 @@ typedef enum bsga_op {
   BSGA_OP_SPECIAL_DENSE_PACKED = 6,
   BSGA_OP_PROBE_SELECT = 7,
   BSGA_OP_NMSE = 8,
-  BSGA_OP_BACKWARD = 9
+  BSGA_OP_BACKWARD = 9,
+  BSGA_OP_PATCH_ROWS_PACKED = 10
 } bsga_op;
 
 /* Shape of one global-attention layer.  head_dim must be 64; block (b) must
@@ -289,16 +290,24 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *   bsga_patch_rows_packed: every patch query attends to the patch tokens of
  *     its kept blocks AND to every special token, in one online softmax, and
  *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
- *     merge in bsga_special_dense, without the intermediate bf16 rounding);
+ *     merge in bsga_special_dense, without the intermediate bf16 rounding).
+ *     Optional workspace (NULL, or bsga_workspace_bytes(
+ *     BSGA_OP_PATCH_ROWS_PACKED) bytes, 0 for b = 64): with it, at b = 128 the
+ *     query blocks left for the last, partial round of workgroups are split
+ *     into pieces of consecutive key tiles whose float32 partials are merged
+ *     by log-sum-exp afterwards, which balances that round; the result is the
+ *     same softmax (it may differ from the unsplit rows in the last bit);
  *   bsga_special_rows_packed: every special query attends to all N tokens
  *     (split over key ranges, partial results combined by log-sum-exp in a
  *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and
  *     writes its row of o/lse.
- * The two calls write disjoint rows and may run in either order. */
+ * The two calls write disjoint rows and may run in either order (with
+ * different workspaces if they overlap). */
 int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q,
                            const void* kv_packed, size_t kv_bytes,
                            const int32_t* row_ptr, const int32_t* col_idx,
-                           uint16_t* o, float* lse, void* stream);
+                           uint16_t* o, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
 int bsga_special_rows_packed(const bsga_shape* shape, const uint16_t* q,
                              const void* kv_packed, size_t kv_bytes,
                              uint16_t* o, float* lse, void* workspace,

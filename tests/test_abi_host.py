@@ -70,7 +70,13 @@ def test_capacity_and_workspace_sizes():
     assert bsga.workspace_bytes(shape, bsga.OP_NMSE) >= 16 * 43 * 16
     out = ctypes.c_size_t()
     assert bsga.workspace_bytes(shape, bsga.OP_BACKWARD) >= 7 * 16 * 44032 * 128
-    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_BACKWARD + 1,
+    # patch rows at b = 128: float32 partials of the last round's split rows
+    # (8 pieces each, fewer than 64 rows per XCD with two workgroups per CU)
+    tail = bsga.workspace_bytes(shape, bsga.OP_PATCH_ROWS_PACKED)
+    assert 128 * 66 * 4 * 8 <= tail <= 8 * 64 * 8 * 128 * 66 * 4 + 256
+    assert bsga.workspace_bytes(shape, bsga.OP_LAYER) >= tail
+    assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PATCH_ROWS_PACKED + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 
 

@@ -422,3 +422,74 @@ def test_end_to_end_mask_vs_oracle_pipeline(lib):
                    if not np.array_equal(ci[rp[r]:rp[r + 1]], oci[orp[r]:orp[r + 1]]))
         say(f"[e2e mask] {name}: {diff} of {rows} rows differ from the float64 pipeline "
             f"(nnz gpu {rp[-1]}, oracle {orp[-1]})")
+
+
+def _split_rows(rows, m, xcds=8):
+    """Rows (head-major query blocks) that the patch-row call at b = 128 runs
+    as key-range pieces: those of each XCD's last, partial round of m
+    workgroup slots (rows are dealt to XCDs in equal contiguous ranges)."""
+    per = -(-rows // xcds)
+    out = []
+    for x in range(xcds):
+        r0 = x * per
+        n_x = min(rows, r0 + per) - r0
+        if n_x <= 0:
+            break
+        full = n_x // m * m
+        out += list(range(r0 + full, r0 + n_x))
+    return out
+
+
+@pytest.mark.parametrize("name", ["vggt-32f", "ragged-b128"])
+def test_patch_rows_tail_pieces(lib, name):
+    """bsga_patch_rows_packed with its workspace splits the rows of the last,
+    partial round into key-range pieces and merges them: those rows (every
+    query) match the oracle within the usual bars, and every other row is
+    byte-identical to the call without workspace (one workgroup per row)."""
+    import torch
+    from gpu_helpers import compare_rows, from_dev_bf16, layer_shape, oracle_rows, say
+    x = inputs(name)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    q, k, v = _upload(x)
+    probs = lib.predict_mask(shape, q, k)
+    row_ptr, col_idx = lib.select(shape, probs, cfg.rho, cfg.tau, x.rho_per_head)
+    kv = lib.pack_kv(shape, k, v)
+    o1, l1 = torch.zeros_like(q), torch.zeros((cfg.heads, cfg.tokens), dtype=torch.float32,
+                                              device=q.device)
+    o2, l2 = torch.zeros_like(o1), torch.zeros_like(l1)
+    lib.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o1, l1, ws=None)
+    lib.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o2, l2)
+    torch.cuda.synchronize()
+    B = lib.num_blocks(shape)
+    m = 2 * torch.cuda.get_device_properties(0).multi_processor_count // 8
+    split = _split_rows(cfg.heads * B, m)
+    say(f"[tail pieces] {name}: {len(split)} of {cfg.heads * B} query blocks split, {m} slots/XCD")
+    assert split, "the shape should leave a partial last round"
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy()[:rp[-1]]
+    _, patch = O.token_roles(cfg.frames, cfg.patches_per_frame, cfg.special_per_frame)
+    tok_of_block = [patch[O.block_members(cfg.n_patch, cfg.block, i)] for i in range(B)]
+    same = torch.ones((cfg.heads, cfg.tokens), dtype=torch.bool, device=q.device)
+    by_head = {}
+    for r in split:
+        h, i = divmod(r, B)
+        by_head.setdefault(h, []).append(i)
+        same[h, torch.from_numpy(tok_of_block[i]).to(q.device)] = False
+    eq = (o1.view(torch.int16) == o2.view(torch.int16)).all(dim=2) & (l1 == l2)
+    assert bool(eq[same].all()), "unsplit rows differ"
+    o2n, l2n = from_dev_bf16(o2), l2.cpu().numpy()
+    worst = worst_l = 0.0
+    acc = cnt = 0.0
+    for h, blocks in sorted(by_head.items()):
+        blocks = blocks[:6]
+        out = oracle_rows(x, h, O.kept_lists(rp, ci, h, B), blocks, special_queries=False)
+        dense = oracle_rows(x, h, None, blocks, special_queries=False)
+        d = np.stack([r[0] for r in dense.values()])
+        acc += float(np.sum(d ** 2))
+        cnt += d.size
+        eo, el, _, _, _ = compare_rows(out, o2n[h], l2n[h])
+        worst, worst_l = max(worst, eo), max(worst_l, el)
+    rms = (acc / cnt) ** 0.5
+    say(f"   split rows: arithmetic err {worst / rms:.3e} rms(O_dense), |dLSE| {worst_l:.1e}")
+    assert worst <= O_TOL * rms and worst_l <= LSE_TOL
