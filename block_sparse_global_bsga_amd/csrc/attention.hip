@@ -53,9 +53,10 @@
 
 namespace bsga {
 
-// kSparse:       patch queries x kept patch blocks (patch-only result)
 // kSparseFused:  patch queries x (kept patch blocks, then every special
-//                tile) in one online softmax: the final patch rows
+//                tile) in one online softmax: the final patch rows; with
+//                AttnArgs::patch_only, the kept patch blocks alone (the
+//                patch-only result)
 // kDense:        every query x every key
 // kSpecialSplit: special queries x a range of key tiles (split-K partials)
 // kPatchSpecial: patch queries x special tiles, merged by log-sum-exp into
@@ -67,7 +68,7 @@ namespace bsga {
 //                over every slot, and concurrent pieces read the same key range
 //                of consecutive rows; tail_merge_kernel combines the pieces
 enum Mode {
-  kSparse = 0, kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5
+  kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5
 };
 
 // pieces per row of the last round (kSparseTail)
@@ -90,6 +91,7 @@ struct AttnArgs {
   int tiles_per_split;
   int rows_per_xcd;  // kSparseTail: rows of each XCD (as xcd_item)
   int tail_m;        // kSparseTail: workgroup slots per XCD (one round)
+  int patch_only;    // kSparseFused: skip the special tiles
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
@@ -97,6 +99,9 @@ struct AttnArgs {
 // in float32 and bf16, and sums over any sequence length stay far below
 // float32 overflow.
 constexpr float kLazySlack = 64.f;
+
+// Fourth word of a raw buffer resource (byte addressing, 32-bit data format)
+constexpr int kBufWord3 = 0x00020000;
 
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).
@@ -149,13 +154,13 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       item = xcd_item(blockIdx.x, a.n_items);
       if (item < 0) return;
     }
-    if constexpr (MODE == kSparse || MODE == kSparseFused || MODE == kSparseTail) {
+    if constexpr (MODE == kSparseFused || MODE == kSparseTail) {
       h = item / d.B;
       qp0 = (item - h * d.B) * QT;
       const int r0 = a.row_ptr[item];
       cols = a.col_idx + r0;
       nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
-      nt = nt_csr * TPB + (MODE == kSparse ? 0 : d.ns_pad / KT);
+      nt = nt_csr * TPB + (a.patch_only ? 0 : d.ns_pad / KT);
     } else if constexpr (MODE == kDense) {
       h = item / a.q_tiles;
       qp0 = (item - h * a.q_tiles) * QT;
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
   // it into the tile's first packed key.  Kept block j of the row covers tiles
   // j TPB .. j TPB + TPB - 1.
-  constexpr bool kCsr = MODE == kSparse || MODE == kSparseFused || MODE == kSparseTail;
+  constexpr bool kCsr = MODE == kSparseFused || MODE == kSparseTail;
   auto tile_raw = [&](int n) -> int {
     if constexpr (kCsr) {
       return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0;
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     raw = __builtin_amdgcn_readfirstlane(raw);
     if constexpr (kCsr) {
       const int nb = nt_csr * TPB;
-      if (MODE != kSparse && n >= nb) return d.np_pad + min(n - nb, d.ns_pad / KT - 1) * KT;
+      if (n >= nb) return d.np_pad + min(n - nb, d.ns_pad / KT - 1) * KT;
       return min(max(raw, 0), d.B - 1) * QT + (n % TPB) * KT;
     } else {
       return (tile0 + n) * KT;
@@ -234,15 +239,24 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       }
     }
   }
+  // Loads go through buffer resources (the head's K rows, the head's V^T
+  // rows): the per-lane part of the address is the 32-bit offset above, the
+  // tile's position a scalar offset, so no 64-bit per-lane addresses are kept.
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  auto set_head = [&](int hd) {
+    kbase = (const char*)a.kp + (size_t)hd * d.ntot_pad * kHeadDim * 2;
+    vbase = (const char*)a.vt + (size_t)hd * kHeadDim * vrow_bytes;
+    krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, d.ntot_pad * kHeadDim * 2, kBufWord3);
+    vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kHeadDim * vrow_bytes, kBufWord3);
+  };
   auto issue_k = [&](int kp0, int slot) {
     lds_u32x4* dst = (lds_u32x4*)&smem[slot * KCH + w * LPW * 64];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int blk = LPW * w + i;  // 64-chunk block of the K tile: rows 8 blk .. 8 blk + 7
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(kbase + (size_t)(kp0 + 8 * blk) * 128 + koff[i & 1]),
-          (__attribute__((address_space(3))) void*)(dst + i * 64), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(dst + i * 64),
+                                               16, koff[i & 1], (kp0 + 8 * blk) * 128, 0, 0);
     }
   };
   auto issue_v = [&](int kp0, int slot) {
@@ -250,70 +264,54 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int blk = LPW * w + i;
-      const size_t row0 = KT == 128 ? 4 * blk : 8 * blk;  // first V^T row of the block
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(vbase + row0 * vrow_bytes + (size_t)kp0 * 2 + voff[i & 3]),
-          (__attribute__((address_space(3))) void*)(dst + i * 64), 16, 0, 0);
+      const int row0 = KT == 128 ? 4 * blk : 8 * blk;  // first V^T row of the block
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(dst + i * 64),
+                                               16, voff[i & 3], row0 * vrow_bytes + kp0 * 2, 0, 0);
     }
   };
 
-  // ---- tile loop.  Before a tile's exponentials, a uniform flag (partial
-  // tile, first tile, or its exact max more than 64 log2 units above the
-  // running max) selects the rare block that masks, takes the exact max and
-  // rescales O and l.
-  bf16x8 qop[4];  // the wave's 32 query rows: lane half hh holds dims [32hh, 32hh + 32)
-  f32x16 o0 = {}, o1 = {};
-  float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units (scores * log2(e)/8)
+  // ---- operand reads.  Per-lane LDS byte offsets within a slot: K rows of
+  // sub-tile 0 for k-step m (sub-tile t adds t * 32 rows); V^T dims l32 at
+  // the keys of (sub-tile t, half h2) (dims 32 + l32 add 32 rows).  With the
+  // slot a compile-time constant every read is one base register plus an
+  // immediate offset.
+  uint32_t kadr[4], vadr[NS][2];
+  {
+    const int R0 = pi_row(l32);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kadr[m] = (uint32_t)(R0 * 8 + ((4 * hh + m) ^ swz_k(R0))) * 16;
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        vadr[t][h2] = (uint32_t)(l32 * VROW + ((4 * t + 2 * h2 + hh) ^ swz_v<KT>(l32))) * 16;
+  }
+  constexpr uint32_t kSlotBytes = KCH * 16, kSubK = 32 * 8 * 16, kVHalf = 32 * VROW * 16;
+  auto lds_op = [&](uint32_t off) -> bf16x8 {
+    return as_bf16x8(*(const u32x4*)((const char*)smem + off));
+  };
 
-  // scores of one 32-key sub-tile t into s, folding them into the running
-  // tile max mx (raw units)
-  auto scores_t = [&](f32x16& s, float& mx, const u32x4* kt, int t) {
-    const int R = 32 * t + pi_row(l32);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const bf16x8 kop = as_bf16x8(kt[R * 8 + ((4 * hh + m) ^ swz_k(R))]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[m], m == 0 ? f32x16{} : s, 0, 0, 0);
-    }
-    // a plain chain: the backend folds it into one v_max3 per two scores
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  };
-  // exponentials of sub-tile t (against the running max) and its P V product.
-  // The sub-tile's four V^T operands are read first and the scheduler may not
-  // sink them (sched_barrier), so the LDS latency hides behind the 16
-  // exponentials instead of stalling each MFMA.
-  auto exp_pv_t = [&](const f32x16& s, float& ls, const u32x4* vt, int t) {
-    bf16x8 va[2], vb[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int ch = 4 * t + 2 * h2 + hh;
-      va[h2] = as_bf16x8(vt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
-      vb[h2] = as_bf16x8(vt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f32x8 e8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        e8[e] = fast_exp2(fmaf(s[8 * h2 + e], kScaleLog2, -m_run));
-        ls += e8[e];
-      }
-      const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pb, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pb, o1, 0, 0, 0);
-    }
-  };
-  // rare block: masking of a partial tile, exact max, rescaling
+  // ---- softmax state of the wave's 32 query rows.  Lane half hh holds
+  // dims [32hh, 32hh + 32) of query row qrow as the B operand, and the
+  // running max (log2 units: scores * log2(e)/8) and sum.
+  bf16x8 qop[4];
+  f32x16 o0, o1;
+  float m_run, l_run;
+  const int qrow = qp0 + 32 * w + l32;
+
+  // Rare block: masking of a partial tile, exact max, rescaling.  Score r of
+  // sub-tile t is key 32 t + pi(8 (r / 4) + 4 hh + r % 4) = kc + 8 hh with
+  // kc = 32 t + 16 (r / 8) + 4 (r / 4 % 2) + r % 4.
   auto rare = [&](f32x16 (&s)[NS], float mx, int valid) {
     if (valid < KT) {
+      const int lim = valid - 8 * hh;
       mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-          if (key >= valid) s[t][r] = -INFINITY;
+          const int kc = 32 * t + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+          if (kc >= lim) s[t][r] = -INFINITY;
           mx = fmaxf(mx, s[t][r]);
         }
     }
@@ -324,21 +322,24 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     l_run *= alpha;
     m_run = m_new;
   };
+  // partial tile, or its exact max (either lane half) more than 64 log2 units
+  // above the running max
   auto needs_rare = [&](float mx, int valid) -> bool {
-    // partial tile, or its exact max (both lane halves) more than 64 log2
-    // units above the running max
     return valid < KT || __any(!(mx * kScaleLog2 - m_run <= kLazySlack));
   };
 
   // Tiles n0 .. n1 - 1 of the current segment, from a fresh softmax state.
-  // CSR entries run two tiles ahead of the compute: the entry of tile n+2 is
-  // loaded during iteration n and consumed after that iteration's closing
-  // wait, so no wait in the middle of an iteration (which would also stall on
-  // the tile prefetch) is needed.  The closing barrier of the last tile also
-  // frees both LDS rings for the next segment.
+  // Tile n sits in LDS slot (n - n0) % 2; iterations come in pairs so the
+  // slot is a compile-time constant.  Per tile the wave computes every score
+  // (the maxima folded in as they come), decides the rare block, then
+  // exponentiates and multiplies by V^T one 32-key sub-tile at a time (the
+  // exponentials of one sub-tile run beside the P V products of the previous
+  // one); the next tile's K and V^T are in flight meanwhile, one barrier per
+  // tile.  CSR entries run two tiles ahead: the entry of tile n+2 is loaded
+  // during iteration n and consumed after that iteration's closing wait.
   auto run_tiles = [&](int n0, int n1) {
     {
-      const int qtok = packed_token(qp0 + 32 * w + l32, d);
+      const int qtok = packed_token(qrow, d);
       const u32x4* src =
           (const u32x4*)(a.q + ((size_t)h * d.n + (qtok < 0 ? 0 : qtok)) * kHeadDim) + 4 * hh;
 #pragma unroll
@@ -348,34 +349,41 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         qop[m] = as_bf16x8(t);
       }
     }
-    kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * kHeadDim * 2;
-    vbase = (const char*)a.vt + (size_t)h * kHeadDim * vrow_bytes;
     o0 = f32x16{};
     o1 = f32x16{};
     m_run = -INFINITY;
     l_run = 0.f;
+    set_head(h);
+    if (n1 <= n0) return;
     int raw_cur = tile_raw(n0), raw_nxt = tile_raw(n0 + 1);
-    if (n1 > n0) {
+    {
       const int kp0 = tile_kp0(n0, raw_cur);
       issue_k(kp0, 0);
       issue_v(kp0, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x16 s[NS];
-    for (int n = n0; n < n1; ++n) {
-      const int slot = (n - n0) & 1;
+    auto step = [&](auto par, int n) {
+      constexpr int P = decltype(par)::value;
+      constexpr uint32_t kb = P * kSlotBytes, vb0 = (2 + P) * kSlotBytes;
       if (n + 1 < n1) {
         const int kp1 = tile_kp0(n + 1, raw_nxt);
-        issue_k(kp1, slot ^ 1);
-        issue_v(kp1, slot ^ 1);
+        issue_k(kp1, P ^ 1);
+        issue_v(kp1, P ^ 1);
       }
       const int raw_after = tile_raw(n + 2);
-      const u32x4* kt = smem + slot * KCH;
-      const u32x4* vt = smem + (2 + slot) * KCH;
+      f32x16 s[NS];
       float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) scores_t(s[t], mx, kt, t);
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kb + kadr[m] + t * kSubK), qop[m],
+                                                         m == 0 ? f32x16{} : s[t], 0, 0, 0);
+        // a plain chain: the backend folds it into one v_max3 per two scores
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      }
       const int valid = tile_valid(tile_kp0(n, raw_cur));
       if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
       float ls = 0.f;
@@ -384,17 +392,46 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       // from starving the VALU
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < NS; ++t) exp_pv_t(s[t], ls, vt, t);
+      for (int t = 0; t < NS; ++t) {
+        // the sub-tile's V^T operands are read first and may not be sunk, so
+        // the LDS latency hides behind the exponentials
+        bf16x8 va[2], vb[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          va[h2] = lds_op(vb0 + vadr[t][h2]);
+          vb[h2] = lds_op(vb0 + vadr[t][h2] + kVHalf);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 e8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            e8[e] = fast_exp2(fmaf(s[t][8 * h2 + e], kScaleLog2, -m_run));
+            ls += e8[e];
+          }
+          const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
+          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pb, o0, 0, 0, 0);
+          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pb, o1, 0, 0, 0);
+        }
+      }
       __builtin_amdgcn_s_setprio(0);
       l_run += ls;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       raw_cur = raw_nxt;
       raw_nxt = raw_after;
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int n = n0;;) {
+      step(std::integral_constant<int, 0>{}, n);
+      if (++n == n1) break;
+      step(std::integral_constant<int, 1>{}, n);
+      if (++n == n1) break;
     }
   };
 
-  // ---- epilogues.  o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query l32].
+  // ---- epilogues.  o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query row qrow].
   // Unnormalised float32 partial of the wave's 32 rows, with the running max
   // (log2 units, or raw-score units if `raw`) and the row sum.
   auto store_partial = [&](float* po_base, float* pml, bool raw) {
@@ -413,7 +450,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   // final rows of O (bf16) and LSE; kPatchSpecial merges into the rows present
   auto store_rows = [&]() {
     const float l_tot = xor32_sum(l_run);
-    const int qtok = packed_token(qp0 + 32 * w + l32, d);
+    const int qtok = packed_token(qrow, d);
     if (qtok < 0) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // natural-log LSE: (m_run + log2 l) ln 2
@@ -465,7 +502,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   } else {
     run_tiles(0, nt);
     if constexpr (MODE == kSpecialSplit) {
-      const int sq = qp0 + 32 * w + l32 - d.np_pad;
+      const int sq = qrow - d.np_pad;
       const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
       // raw-score units for the reduction
       store_partial(a.part_o + slot * kHeadDim, a.part_ml + slot * 2, true);
@@ -603,10 +640,17 @@ hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint
   return hipGetLastError();
 }
 
+// Workgroup shapes: 128-row blocks run four waves over 128-key tiles (64 KB
+// of LDS, two workgroups per compute unit), 64-row blocks two waves over
+// 64-key tiles.
 template <int QT, int KT, int MODE, int WPE = 2>
 static hipError_t run_attn(const AttnArgs& a, hipStream_t st) {
   attn_kernel<QT, KT, MODE, WPE><<<xcd_grid(a.n_items), 2 * QT, 0, st>>>(a);
   return hipGetLastError();
+}
+template <int MODE>
+static hipError_t run_attn_b(const Dims& d, const AttnArgs& a, hipStream_t st) {
+  return d.b == 64 ? run_attn<64, 64, MODE>(a, st) : run_attn<128, 128, MODE>(a, st);
 }
 
 
@@ -629,7 +673,8 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
-  return d.b == 64 ? run_attn<64, 64, kSparse>(a, st) : run_attn<128, 128, kSparse>(a, st);
+  a.patch_only = 1;
+  return run_attn_b<kSparseFused>(d, a, st);
 }
 
 // kSparseTail plan: slots per XCD (two 128 x 128 workgroups per compute unit;
@@ -692,7 +737,7 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       return hipGetLastError();
     }
   }
-  return d.b == 64 ? run_attn<64, 64, kSparseFused>(a, st) : run_attn<128, 128, kSparseFused>(a, st);
+  return run_attn_b<kSparseFused>(d, a, st);
 }
 
 struct SplitPlan {
