@@ -35,13 +35,16 @@
 //  * the first product of each score accumulator starts from the constant 0.
 // Per tile a wave computes all scores, then exponentiates and multiplies by V
 // one 32-key sub-tile at a time (the exponentials of one sub-tile run beside
-// the P V products of the previous one).  The next tile's K and V^T are in
-// flight meanwhile: two LDS slots each, one barrier per tile.
+// the P V products of the previous one).  LDS holds one K tile and one V^T
+// tile: V^T of a tile loads while its scores run, K of the next tile while
+// it is exponentiated, two barriers per tile.  That keeps a 128-row
+// workgroup at 32 KB of LDS and 160 registers per lane, so three waves share
+// each SIMD (three workgroups per compute unit).
 //
 // K and V are first packed (once per layer) into "packed order": patch
 // tokens, padding, special tokens, padding (each segment a multiple of 128),
 // K as rows [H][ntot_pad][64] and V transposed as [H][64][ntot_pad].  Tiles
-// reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes land at
+// reach LDS with buffer_load_dwordx4 ... lds (each lane's 16 bytes land at
 // base + 16 * lane: no staging registers, no LDS store instructions); the
 // bank swizzle is applied on the global side, the lane that fills LDS chunk
 // (row, physical chunk pc) fetching logical chunk pc ^ swizzle(row).  Every
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   constexpr int TPB = QT / KT;
   static_assert(LPW >= 2 && LPW % 2 == 0 && (KT == 64 || LPW % 4 == 0), "tile loads");
   static_assert(TPB >= 1 && QT % KT == 0, "tile shape");
-  __shared__ u32x4 smem[4 * KCH];   // K slots 0, 1 then V^T slots 0, 1
+  __shared__ u32x4 smem[2 * KCH];   // the K tile, then the V^T tile
 
   const Dims& d = a.d;
   const int T = threadIdx.x, lane = T & 63;
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
   };
 
-  // ---- direct-to-LDS tile loads into two rings (K rows, V^T rows), two
-  // slots each.  Every wave issues LPW loads of 64 x 16 B per K tile and LPW
+  // ---- direct-to-LDS tile loads into the K slot and the V^T slot.  Every
+  // wave issues LPW loads of 64 x 16 B per K tile and LPW
   // per V^T tile; load i of wave w fills chunks (LPW w + i) * 64 + lane.
   // The swizzle of the row a lane fills depends on i only through i mod 2
   // (K, and V^T of 64-key tiles) or i mod 4 (V^T of 128-key tiles), so a few
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, d.ntot_pad * kHeadDim * 2, kBufWord3);
     vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kHeadDim * vrow_bytes, kBufWord3);
   };
-  auto issue_k = [&](int kp0, int slot) {
-    lds_u32x4* dst = (lds_u32x4*)&smem[slot * KCH + w * LPW * 64];
+  auto issue_k = [&](int kp0) {
+    lds_u32x4* dst = (lds_u32x4*)&smem[w * LPW * 64];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int blk = LPW * w + i;  // 64-chunk block of the K tile: rows 8 blk .. 8 blk + 7
@@ -259,8 +262,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
                                                16, koff[i & 1], (kp0 + 8 * blk) * 128, 0, 0);
     }
   };
-  auto issue_v = [&](int kp0, int slot) {
-    lds_u32x4* dst = (lds_u32x4*)&smem[(2 + slot) * KCH + w * LPW * 64];
+  auto issue_v = [&](int kp0) {
+    lds_u32x4* dst = (lds_u32x4*)&smem[KCH + w * LPW * 64];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int blk = LPW * w + i;
@@ -272,9 +275,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 
   // ---- operand reads.  Per-lane LDS byte offsets within a slot: K rows of
   // sub-tile 0 for k-step m (sub-tile t adds t * 32 rows); V^T dims l32 at
-  // the keys of (sub-tile t, half h2) (dims 32 + l32 add 32 rows).  With the
-  // slot a compile-time constant every read is one base register plus an
-  // immediate offset.
+  // the keys of (sub-tile t, half h2) (dims 32 + l32 add 32 rows).  Every
+  // read is one base register plus an immediate offset.
   uint32_t kadr[4], vadr[NS][2];
   {
     const int R0 = pi_row(l32);
@@ -329,14 +331,12 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   };
 
   // Tiles n0 .. n1 - 1 of the current segment, from a fresh softmax state.
-  // Tile n sits in LDS slot (n - n0) % 2; iterations come in pairs so the
-  // slot is a compile-time constant.  Per tile the wave computes every score
-  // (the maxima folded in as they come), decides the rare block, then
-  // exponentiates and multiplies by V^T one 32-key sub-tile at a time (the
-  // exponentials of one sub-tile run beside the P V products of the previous
-  // one); the next tile's K and V^T are in flight meanwhile, one barrier per
-  // tile.  CSR entries run two tiles ahead: the entry of tile n+2 is loaded
-  // during iteration n and consumed after that iteration's closing wait.
+  // Per tile the wave computes every score (the maxima folded in as they
+  // come), decides the rare block, then exponentiates and multiplies by V^T
+  // one 32-key sub-tile at a time (the exponentials of one sub-tile run
+  // beside the P V products of the previous one).  CSR entries run two tiles
+  // ahead: the entry of tile n+2 is loaded during iteration n and consumed
+  // after that iteration's waits.
   auto run_tiles = [&](int n0, int n1) {
     {
       const int qtok = packed_token(qrow, d);
@@ -356,21 +356,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     set_head(h);
     if (n1 <= n0) return;
     int raw_cur = tile_raw(n0), raw_nxt = tile_raw(n0 + 1);
-    {
-      const int kp0 = tile_kp0(n0, raw_cur);
-      issue_k(kp0, 0);
-      issue_v(kp0, 0);
-    }
+    issue_k(tile_kp0(n0, raw_cur));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    auto step = [&](auto par, int n) {
-      constexpr int P = decltype(par)::value;
-      constexpr uint32_t kb = P * kSlotBytes, vb0 = (2 + P) * kSlotBytes;
-      if (n + 1 < n1) {
-        const int kp1 = tile_kp0(n + 1, raw_nxt);
-        issue_k(kp1, P ^ 1);
-        issue_v(kp1, P ^ 1);
-      }
+    for (int n = n0; n < n1; ++n) {
+      // V^T(n) fills its slot (free since the previous closing barrier) while
+      // the scores of tile n run
+      const int kp_n = tile_kp0(n, raw_cur);
+      issue_v(kp_n);
       const int raw_after = tile_raw(n + 2);
       f32x16 s[NS];
       float mx = -INFINITY;
@@ -378,18 +371,23 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       for (int t = 0; t < NS; ++t) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kb + kadr[m] + t * kSubK), qop[m],
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kadr[m] + t * kSubK), qop[m],
                                                          m == 0 ? f32x16{} : s[t], 0, 0, 0);
         // a plain chain: the backend folds it into one v_max3 per two scores
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
       }
-      const int valid = tile_valid(tile_kp0(n, raw_cur));
+      const int valid = tile_valid(kp_n);
       if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
+      // V^T(n) has landed and every wave is done with K(n): K(n+1) fills the
+      // K slot while tile n is exponentiated and multiplied by V^T
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (n + 1 < n1) issue_k(tile_kp0(n + 1, raw_nxt));
       float ls = 0.f;
       // the exponential / P V stretch runs at raised issue priority, so that a
-      // wave in it keeps the SIMD's other wave (typically in its score MFMAs)
-      // from starving the VALU
+      // wave in it keeps the SIMD's other waves (typically in their score
+      // MFMAs) from starving the VALU
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
@@ -398,8 +396,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         bf16x8 va[2], vb[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          va[h2] = lds_op(vb0 + vadr[t][h2]);
-          vb[h2] = lds_op(vb0 + vadr[t][h2] + kVHalf);
+          va[h2] = lds_op(kSlotBytes + vadr[t][h2]);
+          vb[h2] = lds_op(kSlotBytes + vadr[t][h2] + kVHalf);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -421,13 +419,6 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       __syncthreads();
       raw_cur = raw_nxt;
       raw_nxt = raw_after;
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int n = n0;;) {
-      step(std::integral_constant<int, 0>{}, n);
-      if (++n == n1) break;
-      step(std::integral_constant<int, 1>{}, n);
-      if (++n == n1) break;
     }
   };
 
@@ -640,10 +631,9 @@ hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint
   return hipGetLastError();
 }
 
-// Workgroup shapes: 128-row blocks run four waves over 128-key tiles (64 KB
-// of LDS, two workgroups per compute unit), 64-row blocks two waves over
-// 64-key tiles.
-template <int QT, int KT, int MODE, int WPE = 2>
+// Workgroup shapes: 128-row blocks run four waves over 128-key tiles (32 KB
+// of LDS), 64-row blocks two waves over 64-key tiles; three waves per SIMD.
+template <int QT, int KT, int MODE, int WPE = 3>
 static hipError_t run_attn(const AttnArgs& a, hipStream_t st) {
   attn_kernel<QT, KT, MODE, WPE><<<xcd_grid(a.n_items), 2 * QT, 0, st>>>(a);
   return hipGetLastError();
@@ -677,8 +667,8 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   return run_attn_b<kSparseFused>(d, a, st);
 }
 
-// kSparseTail plan: slots per XCD (two 128 x 128 workgroups per compute unit;
-// 64 when the device cannot be queried) and the compact slot count of the
+// kSparseTail plan: slots per XCD (three 128 x 128 workgroups per compute
+// unit; 96 when the device cannot be queried) and the compact slot count of the
 // pieces of every XCD's last, partial round.
 struct TailPlan {
   int m, rows, rows_per_xcd, slots, grid;
@@ -686,11 +676,11 @@ struct TailPlan {
 static TailPlan tail_plan(const Dims& d) {
   TailPlan p;
   int dev = 0, cus = 0;
-  p.m = 64;
+  p.m = 96;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       cus >= kXcds / 2)
-    p.m = 2 * cus / kXcds;
+    p.m = 3 * cus / kXcds;
   p.rows = d.H * d.B;
   p.rows_per_xcd = (p.rows + kXcds - 1) / kXcds;
   p.slots = 0;
@@ -729,7 +719,7 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       a.part_ml = (float*)((char*)ws + tail_part_o_bytes(p));
       a.rows_per_xcd = p.rows_per_xcd;
       a.tail_m = p.m;
-      attn_kernel<128, 128, kSparseTail, 2><<<kXcds * p.grid, 256, 0, st>>>(a);
+      attn_kernel<128, 128, kSparseTail, 3><<<kXcds * p.grid, 256, 0, st>>>(a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       tail_merge_kernel<<<dim3(kXcds * p.m, 128 / 4), 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d,
