@@ -65,7 +65,7 @@ namespace bsga {
 // kPatchSpecial: patch queries x special tiles, merged by log-sum-exp into
 //                the patch rows already in O/LSE
 // kSparseTail:   kSparseFused, except that the rows of each XCD's last,
-//                partial round of workgroups are split into kTailPieces pieces
+//                partial round of workgroups are split into tail_pieces pieces
 //                of consecutive key tiles, listed piece-major after the XCD's
 //                whole rows: the in-order dispatch then spreads that round
 //                over every slot, and concurrent pieces read the same key range
@@ -74,8 +74,8 @@ enum Mode {
   kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5
 };
 
-// pieces per row of the last round (kSparseTail)
-constexpr int kTailPieces = 8;
+// most pieces per row of the last round (kSparseTail)
+constexpr int kMaxTailPieces = 16;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -94,6 +94,7 @@ struct AttnArgs {
   int tiles_per_split;
   int rows_per_xcd;  // kSparseTail: rows of each XCD (as xcd_item)
   int tail_m;        // kSparseTail: workgroup slots per XCD (one round)
+  int tail_pieces;   // kSparseTail: pieces per row of the last round
   int patch_only;    // kSparseFused: skip the special tiles
 };
 
@@ -146,12 +147,12 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         item = r0 + j;
       } else {
         const int q = j - full;
-        if (q >= rem * kTailPieces) return;
+        if (q >= rem * a.tail_pieces) return;
         const int t = q % rem;
         piece = q / rem;
         item = r0 + full + t;
         // every XCD before the last holds rows_per_xcd rows
-        piece_slot = ((size_t)x * (a.rows_per_xcd % a.tail_m) + t) * kTailPieces + piece;
+        piece_slot = ((size_t)x * (a.rows_per_xcd % a.tail_m) + t) * a.tail_pieces + piece;
       }
     } else {
       item = xcd_item(blockIdx.x, a.n_items);
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       run_tiles(0, nt);
       store_rows();
     } else {
-      run_tiles(nt * piece / kTailPieces, nt * (piece + 1) / kTailPieces);
+      run_tiles(nt * piece / a.tail_pieces, nt * (piece + 1) / a.tail_pieces);
       const size_t row = piece_slot * QT + 32 * w + l32;
       store_partial(a.part_o + row * kHeadDim, a.part_ml + row * 2, false);
     }
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
 
 // ---------------------------------------------------------------------------
 // Rows that kSparseTail split into pieces: workgroup (XCD x and tail row t,
-// group g of 4 query rows) merges the row's kTailPieces float32 partials by
+// group g of 4 query rows) merges the row's float32 partials by
 // log-sum-exp and writes O and LSE of those queries; thread T owns dimension
 // T % 64 of query 4 g + T / 64.  Many small workgroups keep the partials'
 // reads in flight (the merge is memory-bound).
@@ -542,7 +543,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          const float* __restrict__ part_ml,
                                                          uint16_t* __restrict__ o,
                                                          float* __restrict__ lse, Dims d,
-                                                         int rows, int rows_per_xcd, int m) {
+                                                         int rows, int rows_per_xcd, int m,
+                                                         int pieces) {
   constexpr int QT = 128;
   const int x = blockIdx.x / m, t = blockIdx.x % m;
   const int r0 = x * rows_per_xcd;
@@ -551,12 +553,14 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
   const int full = n_x / m * m, rem = n_x - full;
   if (t >= rem) return;
   const int item = r0 + full + t;
-  const size_t slot0 = ((size_t)x * (rows_per_xcd % m) + t) * kTailPieces;
+  const size_t slot0 = ((size_t)x * (rows_per_xcd % m) + t) * pieces;
   const int T = threadIdx.x, dim = T & 63, qr = 4 * blockIdx.y + (T >> 6);
-  float mi[kTailPieces], li[kTailPieces], oi[kTailPieces];
+  float mi[kMaxTailPieces], li[kMaxTailPieces], oi[kMaxTailPieces];
   float M = -INFINITY;
 #pragma unroll
-  for (int pc = 0; pc < kTailPieces; ++pc) {
+  for (int pc = 0; pc < kMaxTailPieces; ++pc) {
+    mi[pc] = -INFINITY;
+    if (pc >= pieces) continue;
     const size_t row = (slot0 + pc) * QT + qr;
     mi[pc] = part_ml[row * 2];
     li[pc] = part_ml[row * 2 + 1];
@@ -565,7 +569,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
   }
   float acc = 0.f, l = 0.f;
 #pragma unroll
-  for (int pc = 0; pc < kTailPieces; ++pc) {
+  for (int pc = 0; pc < kMaxTailPieces; ++pc) {
     if (mi[pc] == -INFINITY) continue;  // an empty piece, or no key at all
     const float wgt = fast_exp2(mi[pc] - M);
     acc += oi[pc] * wgt;
@@ -671,7 +675,7 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
 // unit; 96 when the device cannot be queried) and the compact slot count of the
 // pieces of every XCD's last, partial round.
 struct TailPlan {
-  int m, rows, rows_per_xcd, slots, grid;
+  int m, rows, rows_per_xcd, pieces, slots, grid;
 };
 static TailPlan tail_plan(const Dims& d) {
   TailPlan p;
@@ -683,16 +687,26 @@ static TailPlan tail_plan(const Dims& d) {
     p.m = 3 * cus / kXcds;
   p.rows = d.H * d.B;
   p.rows_per_xcd = (p.rows + kXcds - 1) / kXcds;
+  p.pieces = 0;
   p.slots = 0;
   p.grid = 0;
+  // as many pieces per row as let the largest last round fit in one round
+  // of slots; a last round more than half full is not split
+  int max_rem = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
+    if (n_x > 0) max_rem = max(max_rem, n_x % p.m);
+  }
+  if (max_rem == 0 || p.m / max_rem < 2) return p;
+  p.pieces = min(kMaxTailPieces, p.m / max_rem);
   for (int x = 0; x < kXcds; ++x) {
     const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
     if (n_x <= 0) break;
     const int full = n_x / p.m * p.m, rem = n_x - full;
     p.slots = x * (p.rows_per_xcd % p.m) + rem;  // the last non-empty XCD's base + its rows
-    p.grid = max(p.grid, full + rem * kTailPieces);
+    p.grid = max(p.grid, full + rem * p.pieces);
   }
-  p.slots *= kTailPieces;
+  p.slots *= p.pieces;
   return p;
 }
 static size_t tail_part_o_bytes(const TailPlan& p) {
@@ -719,11 +733,13 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       a.part_ml = (float*)((char*)ws + tail_part_o_bytes(p));
       a.rows_per_xcd = p.rows_per_xcd;
       a.tail_m = p.m;
+      a.tail_pieces = p.pieces;
       attn_kernel<128, 128, kSparseTail, 3><<<kXcds * p.grid, 256, 0, st>>>(a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       tail_merge_kernel<<<dim3(kXcds * p.m, 128 / 4), 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d,
-                                                                     p.rows, p.rows_per_xcd, p.m);
+                                                                     p.rows, p.rows_per_xcd, p.m,
+                                                                     p.pieces);
       return hipGetLastError();
     }
   }

@@ -292,11 +292,13 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
  *     merge in bsga_special_dense, without the intermediate bf16 rounding).
  *     Optional workspace (NULL, or bsga_workspace_bytes(
- *     BSGA_OP_PATCH_ROWS_PACKED) bytes, 0 for b = 64): with it, at b = 128 the
+ *     BSGA_OP_PATCH_ROWS_PACKED) bytes: 0 for b = 64, and 0 when the last
+ *     round of workgroups is more than half full): with it, at b = 128 the
  *     query blocks left for the last, partial round of workgroups are split
- *     into pieces of consecutive key tiles whose float32 partials are merged
- *     by log-sum-exp afterwards, which balances that round; the result is the
- *     same softmax (it may differ from the unsplit rows in the last bit);
+ *     into pieces of consecutive key tiles (as many per block as let them
+ *     all run at once) whose float32 partials are merged by log-sum-exp
+ *     afterwards, which balances that round; the result is the same softmax
+ *     (it may differ from the unsplit rows in the last bit);
  *   bsga_special_rows_packed: every special query attends to all N tokens
  *     (split over key ranges, partial results combined by log-sum-exp in a
  *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and

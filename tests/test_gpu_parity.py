@@ -429,6 +429,10 @@ def _split_rows(rows, m, xcds=8):
     as key-range pieces: those of each XCD's last, partial round of m
     workgroup slots (rows are dealt to XCDs in equal contiguous ranges)."""
     per = -(-rows // xcds)
+    rems = [(min(rows, (x + 1) * per) - x * per) % m for x in range(xcds)
+            if min(rows, (x + 1) * per) > x * per]
+    if max(rems) == 0 or m // max(rems) < 2:
+        return []  # a last round more than half full is not split
     out = []
     for x in range(xcds):
         r0 = x * per
