@@ -166,37 +166,86 @@ __global__ __launch_bounds__(256) void csr_t_fill_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS tile loads of NW waves.  A row tile (ROWS x 64 bf16) is ROWS*8
-// chunks, chunk (row, pc) filled from logical chunk pc ^ swz_k(row); a
-// transposed tile (64 dims x T tokens) is 64 * T/8 chunks, chunk (dim, pc)
-// from logical chunk pc ^ swz_v<T>(dim).
+// Direct-to-LDS tile loads of NW waves through buffer resources.  A row tile
+// (ROWS x 64 bf16) is ROWS*8 chunks, chunk (row, pc) filled from logical
+// chunk pc ^ swz_k(row); a transposed tile (64 dims x 64 tokens) is 64*8
+// chunks, chunk (dim, pc) from logical chunk pc ^ swz_v<64>(dim).  Load i of
+// wave w fills the 64 chunks of block LPW w + i (rows or dims 8 blk .. 8 blk
+// + 7); both swizzles depend on the block only through its parity, so two
+// per-lane byte offsets per tile kind cover every load, and the block's
+// position is a scalar offset.
+struct TileOffsets {
+  uint32_t row[2], col[2];
+};
+__device__ inline TileOffsets tile_offsets(int lane, uint32_t col_row_bytes) {
+  TileOffsets o;
+  const int r = lane >> 3, pc = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    o.row[j] = (uint32_t)(r * 128 + 16 * (pc ^ swz_k(8 * j + r)));
+    o.col[j] = (uint32_t)r * col_row_bytes + 16 * (pc ^ swz_v<64>(8 * j + r));
+  }
+  return o;
+}
+// Fourth word of a raw buffer resource (byte addressing, 32-bit data format)
+constexpr int kBufWord3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
+}
 template <int ROWS, int NW>
-__device__ inline void load_rows(const char* head_base, int row0, u32x4* lds, int w, int lane) {
+__device__ inline void load_rows(__amdgpu_buffer_rsrc_t rs, const TileOffsets& to, int row0,
+                                 u32x4* lds, int w) {
   constexpr int LPW = ROWS * 8 / (64 * NW);
+  static_assert(LPW >= 1 && (LPW == 1 || LPW % 2 == 0), "row tile loads");
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int blk = LPW * w + i;
-    const int row = 8 * blk + (lane >> 3), pc = lane & 7;
-    const char* src = head_base + (size_t)(row0 + row) * 128 + 16 * (pc ^ swz_k(row));
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
+                                             to.row[blk & 1], (row0 + 8 * blk) * 128, 0, 0);
   }
 }
-template <int T, int NW>
-__device__ inline void load_cols(const char* head_base, uint32_t row_bytes, int col0, u32x4* lds,
-                                 int w, int lane) {
-  constexpr int LPW = T * 8 / (64 * NW);
-  constexpr int CPR = T / 8;       // chunks per dim row
-  constexpr int RPB = 64 / CPR;    // dim rows per 64-chunk block
+template <int NW>
+__device__ inline void load_cols(__amdgpu_buffer_rsrc_t rs, const TileOffsets& to,
+                                 uint32_t row_bytes, int col0, u32x4* lds, int w) {
+  constexpr int LPW = 8 / NW;  // 64 dims x 8 chunks = 8 blocks of 64 chunks
+  static_assert(LPW >= 1 && (LPW == 1 || LPW % 2 == 0), "column tile loads");
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int blk = LPW * w + i;
-    const int dim = RPB * blk + lane / CPR, pc = lane % CPR;
-    const char* src = head_base + (size_t)dim * row_bytes + (size_t)col0 * 2 + 16 * (pc ^ swz_v<T>(dim));
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((lds_u32x4*)lds + blk * 64), 16,
+                                             to.col[blk & 1], 8 * blk * row_bytes + col0 * 2, 0, 0);
   }
 }
+
+// Per-lane LDS byte offsets of the MFMA A operands within a tile: row tiles
+// (K, V, Q, dO rows) at sub-tile 0 and k-step m, sub-tile t adding t * 32
+// rows; transposed 64-token tiles at the tokens of (sub-tile t, half h2) for
+// dims l32, dims 32 + l32 adding 32 rows.  With the tile's slot a
+// compile-time constant every operand read is a base register plus an
+// immediate offset.
+struct OperandOffsets {
+  uint32_t row[4], col[2][2];
+};
+__device__ inline OperandOffsets operand_offsets(int l32, int hh) {
+  OperandOffsets o;
+  const int R0 = pi_row(l32);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o.row[m] = (uint32_t)(R0 * 8 + ((4 * hh + m) ^ swz_k(R0))) * 16;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      o.col[t][h2] = (uint32_t)(l32 * 8 + ((4 * t + 2 * h2 + hh) ^ swz_v<64>(l32))) * 16;
+  return o;
+}
+constexpr uint32_t kSubRows = 32 * 8 * 16;   // 32 rows of a row tile, bytes
+constexpr uint32_t kHalfCols = 32 * 8 * 16;  // 32 dims of a transposed 64-token tile, bytes
+__device__ inline bf16x8 lds_op(const u32x4* smem, uint32_t off) {
+  return as_bf16x8(*(const u32x4*)((const char*)smem + off));
+}
+// Score r of a lane's 32-row sub-tile accumulator is row pi(8 (r / 4) + 4 hh
+// + r % 4) = kc(r) + 8 hh of the sub-tile.
+__device__ constexpr int acc_row(int r) { return 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3); }
 
 struct BwdArgs {
   const uint16_t* qp;   // packed rows
@@ -222,12 +271,15 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------------------
 // dQ: QT queries per workgroup (one patch block, or a tile of special
-// queries), KT-key tiles: the kept blocks (TPB tiles each) then the special
+// queries), 64-key tiles: the kept blocks (TPB tiles each) then the special
 // tiles for patch queries, every tile for special queries.
-template <int QT, int KT>
-__global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+// 128-row workgroups run three waves per SIMD (48 KB of LDS each, 168 VGPRs).
+template <int QT>
+__global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 128 ? 3 : 2,
+                                                                         QT == 128 ? 3 : 2))) void dq_kernel(
     BwdArgs a) {
-  constexpr int NW = QT / 32, NS = KT / 32, VROW = KT / 8, KCH = 8 * KT, TPB = QT / KT;
+  constexpr int KT = 64, NW = QT / 32, NS = KT / 32, KCH = 8 * KT, TPB = QT / KT;
+  constexpr uint32_t kTile = KCH * 16;   // bytes of one tile
   __shared__ u32x4 smem[2 * 3 * KCH];  // slot s: K rows, V rows, K^T
   const Dims& d = a.d;
   const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, a.n_items));
@@ -278,15 +330,18 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   const float lse2 = a.lse2[(size_t)h * d.ntot_pad + qrow];
 
-  const char* kbase = (const char*)a.kp + (size_t)h * d.ntot_pad * 128;
-  const char* vbase = (const char*)a.vp + (size_t)h * d.ntot_pad * 128;
   const uint32_t trow = (uint32_t)d.ntot_pad * 2;
-  const char* ktbase = (const char*)a.kt + (size_t)h * 64 * trow;
+  const uint32_t head_rows = (uint32_t)d.ntot_pad * 128;
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc((const char*)a.kp + (size_t)h * head_rows, head_rows);
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc((const char*)a.vp + (size_t)h * head_rows, head_rows);
+  const __amdgpu_buffer_rsrc_t ktrs = buf_rsrc((const char*)a.kt + (size_t)h * 64 * trow, 64 * trow);
+  const TileOffsets to = tile_offsets(lane, trow);
+  const OperandOffsets op = operand_offsets(l32, hh);
   auto issue = [&](int kp0, int slot, bool with_kt) {
     u32x4* base = smem + slot * 3 * KCH;
-    load_rows<KT, NW>(kbase, kp0, base, w, lane);
-    load_rows<KT, NW>(vbase, kp0, base + KCH, w, lane);
-    if (with_kt) load_cols<KT, NW>(ktbase, trow, kp0, base + 2 * KCH, w, lane);
+    load_rows<KT, NW>(krs, to, kp0, base, w);
+    load_rows<KT, NW>(vrs, to, kp0, base + KCH, w);
+    if (with_kt) load_cols<NW>(ktrs, to, trow, kp0, base + 2 * KCH, w);
   };
 
   // Two sweeps over the key tiles.  The first accumulates D = sum_k P dP,
@@ -295,43 +350,44 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // rounding (D from the stored bf16 O would not, and the gradients of a
   // peaked softmax are exactly such small differences).  The second sweep
   // forms dS = P (dP - D) and feeds it to the dQ product as a bf16 pair
-  // hi + lo (16 significant bits), for the same reason.
+  // hi + lo (16 significant bits), for the same reason.  Tiles alternate
+  // between two LDS slots; iterations come in pairs so the slot is a
+  // compile-time constant.
   f32x16 g0 = {}, g1 = {};  // dQ^T: dims 0-31 and 32-63 x the wave's 32 queries
   float d_lane = 0.f, dq_d = 0.f;
   for (int sweep = 0; sweep < 2; ++sweep) {
     const bool second = sweep == 1;
+    if (nt == 0) break;
     int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
-    if (nt > 0) issue(tile_kp0(0, raw_cur), 0, second);
+    issue(tile_kp0(0, raw_cur), 0, second);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int n = 0; n < nt; ++n) {
-      const int slot = n & 1;
-      if (n + 1 < nt) issue(tile_kp0(n + 1, raw_nxt), slot ^ 1, second);
+    auto step = [&](auto par, int n) {
+      constexpr int P = decltype(par)::value;
+      constexpr uint32_t kb = P * 3 * kTile, vb = kb + kTile, ktb = kb + 2 * kTile;
+      if (n + 1 < nt) issue(tile_kp0(n + 1, raw_nxt), P ^ 1, second);
       const int raw_after = tile_raw(n + 2);
-      const u32x4* kt = smem + slot * 3 * KCH;
-      const u32x4* vt = kt + KCH;
-      const u32x4* ktt = kt + 2 * KCH;
       const int valid = tile_valid(tile_kp0(n, raw_cur));
       // only a partial tile (the last patch block, the last special tile)
       // masks keys past its end; full tiles run the same code without it
       auto tile = [&](auto full_tag) {
         constexpr bool kFull = decltype(full_tag)::value;
+        const int lim = valid - 8 * hh;  // key acc_row(r) + 8 hh of a sub-tile t is kept iff 32 t + acc_row(r) < lim
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-          const int R = 32 * t + pi_row(l32);
           f32x16 s = {}, dp = {};
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kt[c]), qop[m], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vt[c]), dop[m], dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(smem, kb + op.row[m] + t * kSubRows),
+                                                        qop[m], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(smem, vb + op.row[m] + t * kSubRows),
+                                                         dop[m], dp, 0, 0, 0);
           }
           if (!second) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
               const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
-              d_lane = fmaf((kFull || key < valid) ? p : 0.f, dp[r], d_lane);
+              d_lane = fmaf((kFull || 32 * t + acc_row(r) < lim) ? p : 0.f, dp[r], d_lane);
             }
             continue;
           }
@@ -342,16 +398,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * h2 + e;
               const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
-              const int key = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-              e8[e] = (kFull || key < valid) ? p * (dp[r] - dq_d) : 0.f;
+              e8[e] = (kFull || 32 * t + acc_row(r) < lim) ? p * (dp[r] - dq_d) : 0.f;
             }
             const bf16x8 ds_hi = __builtin_convertvector(e8, bf16x8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)ds_hi[e];
             const bf16x8 ds_lo = __builtin_convertvector(rem, bf16x8);
-            const int ch = 4 * t + 2 * h2 + hh;
-            const bf16x8 k0 = as_bf16x8(ktt[l32 * VROW + (ch ^ swz_v<KT>(l32))]);
-            const bf16x8 k1 = as_bf16x8(ktt[(32 + l32) * VROW + (ch ^ swz_v<KT>(32 + l32))]);
+            const bf16x8 k0 = lds_op(smem, ktb + op.col[t][h2]);
+            const bf16x8 k1 = lds_op(smem, ktb + op.col[t][h2] + kHalfCols);
             g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_hi, g0, 0, 0, 0);
             g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_hi, g1, 0, 0, 0);
             g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
@@ -365,12 +419,19 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       __syncthreads();
       raw_cur = raw_nxt;
       raw_nxt = raw_after;
+    };
+    for (int n = 0;;) {
+      step(std::integral_constant<int, 0>{}, n);
+      if (++n == nt) break;
+      step(std::integral_constant<int, 1>{}, n);
+      if (++n == nt) break;
     }
     if (!second) {
       dq_d = xor32_sum(d_lane);  // lanes l and l + 32 hold the same query
       if (hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = dq_d;
     }
   }
+  if (nt == 0 && hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = 0.f;
   const int tok = packed_token(qrow, d);
   if (tok < 0) return;
   float* out = a.dq + ((size_t)h * d.n + tok) * kHeadDim;
@@ -385,14 +446,15 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
 // ---------------------------------------------------------------------------
 // dK, dV: KT keys per workgroup (one patch block, or a tile of special keys),
-// QT-query tiles: for a patch key block the query blocks that keep it (from
+// 64-query tiles: for a patch key block the query blocks that keep it (from
 // the transposed CSR, QPB tiles each) then every special query tile; for
 // special keys every query tile.
-template <int KT, int QT>
+template <int KT>
 __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64, KT / 64))) void dkdv_kernel(
     BwdArgs a, int qpb) {
-  constexpr int NW = KT / 32, NS = QT / 32, VROW = QT / 8, QCH = 8 * QT;
-  static_assert(QT == 64 && NW >= 2, "one 64-lane load per statistics row");
+  constexpr int QT = 64, NW = KT / 32, NS = QT / 32, QCH = 8 * QT;
+  constexpr uint32_t kTile = QCH * 16;
+  static_assert(NW >= 2, "one 64-lane load per statistics row");
   // slot s: Q rows, dO rows, Q^T, dO^T, then lse2 and D
   __shared__ u32x4 smem[2 * 4 * QCH];
   __shared__ float stats[2][2][QT];
@@ -442,17 +504,20 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
   }
 
   const size_t hrow = (size_t)h * d.ntot_pad;
-  const char* qbase = (const char*)a.qp + hrow * 128;
-  const char* obase = (const char*)a.dop + hrow * 128;
   const uint32_t trow = (uint32_t)d.ntot_pad * 2;
-  const char* qtbase = (const char*)a.qt + (size_t)h * 64 * trow;
-  const char* otbase = (const char*)a.dot + (size_t)h * 64 * trow;
+  const uint32_t head_rows = (uint32_t)d.ntot_pad * 128;
+  const __amdgpu_buffer_rsrc_t qrs = buf_rsrc((const char*)a.qp + hrow * 128, head_rows);
+  const __amdgpu_buffer_rsrc_t ors = buf_rsrc((const char*)a.dop + hrow * 128, head_rows);
+  const __amdgpu_buffer_rsrc_t qtrs = buf_rsrc((const char*)a.qt + (size_t)h * 64 * trow, 64 * trow);
+  const __amdgpu_buffer_rsrc_t otrs = buf_rsrc((const char*)a.dot + (size_t)h * 64 * trow, 64 * trow);
+  const TileOffsets to = tile_offsets(lane, trow);
+  const OperandOffsets op = operand_offsets(l32, hh);
   auto issue = [&](int qp0, int slot) {
     u32x4* base = smem + slot * 4 * QCH;
-    load_rows<QT, NW>(qbase, qp0, base, w, lane);
-    load_rows<QT, NW>(obase, qp0, base + QCH, w, lane);
-    load_cols<QT, NW>(qtbase, trow, qp0, base + 2 * QCH, w, lane);
-    load_cols<QT, NW>(otbase, trow, qp0, base + 3 * QCH, w, lane);
+    load_rows<QT, NW>(qrs, to, qp0, base, w);
+    load_rows<QT, NW>(ors, to, qp0, base + QCH, w);
+    load_cols<NW>(qtrs, to, trow, qp0, base + 2 * QCH, w);
+    load_cols<NW>(otrs, to, trow, qp0, base + 3 * QCH, w);
     // lse2 and D of the tile's 64 queries: one 4-byte direct-to-LDS load per
     // lane, issued by waves 0 and 1 (no register round trip, no extra wait)
     if (w < 2)
@@ -460,73 +525,81 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
                                        (lds_void*)&stats[slot][w][0], 4, 0, 0);
   };
 
+  // Query tiles alternate between two LDS slots; iterations come in pairs so
+  // the slot is a compile-time constant.
   f32x16 v0 = {}, v1 = {}, k0 = {}, k1 = {};  // dV^T, dK^T: dims x the wave's 32 keys
-  int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
-  if (nt > 0) issue(tile_qp0(0, raw_cur), 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int n = 0; n < nt; ++n) {
-    const int slot = n & 1;
-    if (n + 1 < nt) issue(tile_qp0(n + 1, raw_nxt), slot ^ 1);
-    const int raw_after = tile_raw(n + 2);
-    const u32x4* qr = smem + slot * 4 * QCH;
-    const u32x4* orr = qr + QCH;
-    const u32x4* qtt = qr + 2 * QCH;
-    const u32x4* ott = qr + 3 * QCH;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      const int R = 32 * t + pi_row(l32);
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int c = R * 8 + ((4 * hh + m) ^ swz_k(R));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qr[c]), kop[m], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(orr[c]), vop[m], dp, 0, 0, 0);
-      }
-      // accumulator row i of this lane holds query 32t + pi(i), i = 8(r/4) + 4hh + r%4
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        f32x8 p8, s8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * h2 + e;
-          const int qq = 32 * t + pi_row(8 * (r >> 2) + 4 * hh + (r & 3));
-          const float p = fast_exp2(fmaf(s[r], kScaleLog2, -stats[slot][0][qq]));
-          p8[e] = p;
-          s8[e] = p * (dp[r] - stats[slot][1][qq]);
-        }
-        // P and dS enter the products as bf16 pairs hi + lo: dV and dK of a
-        // key sum thousands of weighted rows, and a single bf16 rounding of
-        // each weight would dominate their error
-        const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
-        const bf16x8 sb = __builtin_convertvector(s8, bf16x8);
-        f32x8 prem, rem;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          prem[e] = p8[e] - (float)pb[e];
-          rem[e] = s8[e] - (float)sb[e];
-        }
-        const bf16x8 pl = __builtin_convertvector(prem, bf16x8);
-        const bf16x8 sl = __builtin_convertvector(rem, bf16x8);
-        const int ch = 4 * t + 2 * h2 + hh;
-        const bf16x8 o0 = as_bf16x8(ott[l32 * VROW + (ch ^ swz_v<QT>(l32))]);
-        const bf16x8 o1 = as_bf16x8(ott[(32 + l32) * VROW + (ch ^ swz_v<QT>(32 + l32))]);
-        const bf16x8 q0 = as_bf16x8(qtt[l32 * VROW + (ch ^ swz_v<QT>(l32))]);
-        const bf16x8 q1 = as_bf16x8(qtt[(32 + l32) * VROW + (ch ^ swz_v<QT>(32 + l32))]);
-        v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pb, v0, 0, 0, 0);
-        v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pb, v1, 0, 0, 0);
-        v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pl, v0, 0, 0, 0);
-        v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pl, v1, 0, 0, 0);
-        k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sb, k0, 0, 0, 0);
-        k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sb, k1, 0, 0, 0);
-        k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sl, k0, 0, 0, 0);
-        k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sl, k1, 0, 0, 0);
-      }
-    }
+  if (nt > 0) {
+    int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
+    issue(tile_qp0(0, raw_cur), 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    raw_cur = raw_nxt;
-    raw_nxt = raw_after;
+    auto step = [&](auto par, int n) {
+      constexpr int P = decltype(par)::value;
+      constexpr uint32_t qb = P * 4 * kTile, ob = qb + kTile, qtb = qb + 2 * kTile, otb = qb + 3 * kTile;
+      if (n + 1 < nt) issue(tile_qp0(n + 1, raw_nxt), P ^ 1);
+      const int raw_after = tile_raw(n + 2);
+      const float* lse_t = stats[P][0] + 8 * hh;
+      const float* dd_t = stats[P][1] + 8 * hh;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(smem, qb + op.row[m] + t * kSubRows),
+                                                      kop[m], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(smem, ob + op.row[m] + t * kSubRows),
+                                                       vop[m], dp, 0, 0, 0);
+        }
+        // accumulator entry r of this lane is query 32 t + acc_row(r) + 8 hh
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 p8, s8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h2 + e;
+            const int qq = 32 * t + acc_row(r);
+            const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse_t[qq]));
+            p8[e] = p;
+            s8[e] = p * (dp[r] - dd_t[qq]);
+          }
+          // P and dS enter the products as bf16 pairs hi + lo: dV and dK of a
+          // key sum thousands of weighted rows, and a single bf16 rounding of
+          // each weight would dominate their error
+          const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+          const bf16x8 sb = __builtin_convertvector(s8, bf16x8);
+          f32x8 prem, rem;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            prem[e] = p8[e] - (float)pb[e];
+            rem[e] = s8[e] - (float)sb[e];
+          }
+          const bf16x8 pl = __builtin_convertvector(prem, bf16x8);
+          const bf16x8 sl = __builtin_convertvector(rem, bf16x8);
+          const bf16x8 o0 = lds_op(smem, otb + op.col[t][h2]);
+          const bf16x8 o1 = lds_op(smem, otb + op.col[t][h2] + kHalfCols);
+          const bf16x8 q0 = lds_op(smem, qtb + op.col[t][h2]);
+          const bf16x8 q1 = lds_op(smem, qtb + op.col[t][h2] + kHalfCols);
+          v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pb, v0, 0, 0, 0);
+          v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pb, v1, 0, 0, 0);
+          v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pl, v0, 0, 0, 0);
+          v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pl, v1, 0, 0, 0);
+          k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sb, k0, 0, 0, 0);
+          k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sb, k1, 0, 0, 0);
+          k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sl, k0, 0, 0, 0);
+          k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sl, k1, 0, 0, 0);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      raw_cur = raw_nxt;
+      raw_nxt = raw_after;
+    };
+    for (int n = 0;;) {
+      step(std::integral_constant<int, 0>{}, n);
+      if (++n == nt) break;
+      step(std::integral_constant<int, 1>{}, n);
+      if (++n == nt) break;
+    }
   }
   const int tok = packed_token(krow, d);
   if (tok < 0) return;
@@ -594,14 +667,14 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
   a.t_ptr = t_ptr; a.t_list = t_list; a.dq = dq; a.dk = dk; a.dv = dv; a.d = d;
   if (d.b == 128) {
     a.n_items = d.H * (d.B + d.ns_pad / 128);
-    dq_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+    dq_kernel<128><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 128);
-    dkdv_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
+    dkdv_kernel<128><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
   } else {
     a.n_items = d.H * (d.B + d.ns_pad / 64);
-    dq_kernel<64, 64><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
+    dq_kernel<64><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 64);
-    dkdv_kernel<64, 64><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 1);
+    dkdv_kernel<64><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 1);
   }
   return hipGetLastError();
 }
