@@ -38,8 +38,8 @@
 // the P V products of the previous one).  LDS holds one K tile and one V^T
 // tile: V^T of a tile loads while its scores run, K of the next tile while
 // it is exponentiated, two barriers per tile.  That keeps a 128-row
-// workgroup at 32 KB of LDS and 160 registers per lane, so three waves share
-// each SIMD (three workgroups per compute unit).
+// workgroup at 32 KB of LDS and at most 168 registers per lane, so three
+// waves share each SIMD (three workgroups per compute unit).
 //
 // K and V are first packed (once per layer) into "packed order": patch
 // tokens, padding, special tokens, padding (each segment a multiple of 128),
@@ -219,12 +219,11 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   };
 
   // ---- direct-to-LDS tile loads into the K slot and the V^T slot.  Every
-  // wave issues LPW loads of 64 x 16 B per K tile and LPW
-  // per V^T tile; load i of wave w fills chunks (LPW w + i) * 64 + lane.
-  // The swizzle of the row a lane fills depends on i only through i mod 2
-  // (K, and V^T of 64-key tiles) or i mod 4 (V^T of 128-key tiles), so a few
-  // per-lane byte offsets cover all loads.  Addresses are a uniform base
-  // (scalar registers, the head's) plus a 32-bit per-lane offset.
+  // wave issues LPW loads of 64 x 16 B per K tile and LPW per V^T tile; load
+  // i of wave w fills chunks (LPW w + i) * 64 + lane.  The swizzle of the row
+  // a lane fills depends on i only through i mod 2 (K, and V^T of 64-key
+  // tiles) or i mod 4 (V^T of 128-key tiles), so a few per-lane byte offsets
+  // cover all loads.
   const uint32_t vrow_bytes = (uint32_t)d.ntot_pad * 2;
   const char* kbase = nullptr;
   const char* vbase = nullptr;
