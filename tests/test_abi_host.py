@@ -58,6 +58,20 @@ def test_keep_count_matches_oracle_definition():
         assert bsga.keep_count(B, rho) == O.keep_count(B, rho)
 
 
+def tail_bytes(rows, m=96, xcds=8, max_pieces=16):
+    """Workspace of the split last round, as the plan defines it: rows dealt
+    to XCDs in equal contiguous ranges, m slots per XCD, as many pieces per
+    leftover row as fit one round (at most max_pieces; none when the largest
+    leftover exceeds half a round)."""
+    per = -(-rows // xcds)
+    rems = [(min(rows, (x + 1) * per) - x * per) % m for x in range(xcds)
+            if min(rows, (x + 1) * per) > x * per]
+    if max(rems) == 0 or m // max(rems) < 2:
+        return 0
+    pieces = min(max_pieces, m // max(rems))
+    return sum(rems) * pieces * 128 * 66 * 4
+
+
 def test_capacity_and_workspace_sizes():
     shape = S(32, 1369, 5, 16, 128)
     assert bsga.csr_capacity(shape) == 16 * 343 * 343
@@ -70,12 +84,25 @@ def test_capacity_and_workspace_sizes():
     assert bsga.workspace_bytes(shape, bsga.OP_NMSE) >= 16 * 43 * 16
     out = ctypes.c_size_t()
     assert bsga.workspace_bytes(shape, bsga.OP_BACKWARD) >= 7 * 16 * 44032 * 128
-    # patch rows at b = 128: float32 partials of the last round's split rows
-    # (8 pieces each, fewer than 64 rows per XCD with two workgroups per CU)
+    # patch rows at b = 128: float32 partials (64 values, max and sum per
+    # query) of the last round's split rows.  Without a device the plan
+    # assumes 96 workgroup slots per XCD: 5488 rows are 686 per XCD, 14 of
+    # them in the last round, split into 96 // 14 = 6 pieces each
     tail = bsga.workspace_bytes(shape, bsga.OP_PATCH_ROWS_PACKED)
-    assert 128 * 66 * 4 * 8 <= tail <= 8 * 64 * 8 * 128 * 66 * 4 + 256
+    assert tail_bytes(5488) == 8 * 14 * 6 * 128 * 66 * 4
+    assert tail_bytes(5488) <= tail <= tail_bytes(5488) + 512
     assert bsga.workspace_bytes(shape, bsga.OP_LAYER) >= tail
     assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    # 400 rows: 50 per XCD, a last round more than half full is not split
+    assert bsga.workspace_bytes(S(1, 3200, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    # 8 rows: one per XCD, split into the most pieces (16)
+    assert tail_bytes(8) == 8 * 1 * 16 * 128 * 66 * 4
+    assert tail_bytes(8) <= bsga.workspace_bytes(S(1, 1024, 5, 1, 128),
+                                                 bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(8) + 512
+    # 64 rows: 8 per XCD, 96 // 8 = 12 pieces
+    assert tail_bytes(64) == 8 * 8 * 12 * 128 * 66 * 4
+    assert tail_bytes(64) <= bsga.workspace_bytes(S(1, 1024, 5, 8, 128),
+                                                  bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(64) + 512
     assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PATCH_ROWS_PACKED + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 

@@ -497,3 +497,32 @@ def test_patch_rows_tail_pieces(lib, name):
     rms = (acc / cnt) ** 0.5
     say(f"   split rows: arithmetic err {worst / rms:.3e} rms(O_dense), |dLSE| {worst_l:.1e}")
     assert worst <= O_TOL * rms and worst_l <= LSE_TOL
+
+
+def test_patch_rows_unsplit_when_last_round_large(lib):
+    """400 query blocks (16 heads x 25) leave 50 per XCD for the last round of
+    96 slots: more than half a round, so the plan splits nothing, the
+    workspace is empty, and the call with a workspace is byte-identical to
+    the one without."""
+    import torch
+    from gpu_helpers import layer_shape, say
+    x = synth.random_layer(1, 40, 80, 16, 128, seed=21)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    B = lib.num_blocks(shape)
+    m = 3 * torch.cuda.get_device_properties(0).multi_processor_count // 8
+    if _split_rows(cfg.heads * B, m):
+        pytest.skip(f"{m} slots per XCD split this shape")
+    assert lib.workspace_bytes(shape, lib.OP_PATCH_ROWS_PACKED) <= 1
+    q, k, v = _upload(x)
+    probs = lib.predict_mask(shape, q, k)
+    row_ptr, col_idx = lib.select(shape, probs, cfg.rho, cfg.tau)
+    kv = lib.pack_kv(shape, k, v)
+    o1, l1 = torch.zeros_like(q), torch.zeros((cfg.heads, cfg.tokens), dtype=torch.float32,
+                                              device=q.device)
+    o2, l2 = torch.zeros_like(o1), torch.zeros_like(l1)
+    lib.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o1, l1, ws=None)
+    lib.patch_rows_packed(shape, q, kv, row_ptr, col_idx, o2, l2)
+    torch.cuda.synchronize()
+    say(f"[unsplit last round] {cfg.heads * B} query blocks, {m} slots/XCD")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
