@@ -253,7 +253,10 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, d.ntot_pad * kHeadDim * 2, kBufWord3);
     vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kHeadDim * vrow_bytes, kBufWord3);
   };
+  // (the tile position is wave-uniform; readfirstlane keeps it a scalar
+  // offset, so each load is one instruction)
   auto issue_k = [&](int kp0) {
+    kp0 = __builtin_amdgcn_readfirstlane(kp0);
     lds_u32x4* dst = (lds_u32x4*)&smem[w * LPW * 64];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -263,6 +266,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     }
   };
   auto issue_v = [&](int kp0) {
+    kp0 = __builtin_amdgcn_readfirstlane(kp0);
     lds_u32x4* dst = (lds_u32x4*)&smem[KCH + w * LPW * 64];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
