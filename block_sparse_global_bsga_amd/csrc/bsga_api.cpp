@@ -41,10 +41,11 @@ int check_shape(const bsga_shape* s) {
     return BSGA_ERR_INVALID_ARG;
   if (s->head_dim != kHeadDim) return BSGA_ERR_UNSUPPORTED;
   if (s->block != 64 && s->block != 128) return BSGA_ERR_UNSUPPORTED;
-  // 32-bit token and packed indices inside the kernels
+  // 32-bit byte offsets within one head inside the kernels: a head's padded
+  // [tokens][64] bf16 array must stay below 2 GB (about 16.7 million tokens)
   const int64_t n = (int64_t)s->frames * ((int64_t)s->patches_per_frame + s->special_per_frame);
   const int64_t npad = n + 2 * kPad;
-  if (npad * kHeadDim >= ((int64_t)1 << 31)) return BSGA_ERR_UNSUPPORTED;
+  if (npad * kHeadDim * 2 >= ((int64_t)1 << 31)) return BSGA_ERR_UNSUPPORTED;
   const int64_t np = (int64_t)s->frames * s->patches_per_frame;
   const int64_t B = (np + s->block - 1) / s->block;
   if ((int64_t)s->heads * B >= ((int64_t)1 << 31)) return BSGA_ERR_UNSUPPORTED;

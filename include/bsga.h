@@ -54,7 +54,8 @@ extern "C" {
 typedef enum bsga_status {
   BSGA_OK = 0,
   BSGA_ERR_INVALID_ARG = 1, /* null pointer, bad size, rho/tau out of range */
-  BSGA_ERR_UNSUPPORTED = 2, /* head_dim != 64, block not 64/128, too large */
+  BSGA_ERR_UNSUPPORTED = 2, /* head_dim != 64, block not 64/128, too large
+                               (N + 256 >= 2^24 tokens, or a select limit) */
   BSGA_ERR_MISALIGNED = 3,  /* bf16 tensors not 16-byte aligned, others 4 */
   BSGA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small */
   BSGA_ERR_HIP = 5          /* a kernel launch failed */

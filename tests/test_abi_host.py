@@ -136,9 +136,13 @@ def test_invalid_shapes_rejected():
     s = S(1, 10, 5, 1, 64, head_dim=128)
     assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
     assert lib.bsga_num_blocks(None, ctypes.byref(out)) == bsga.ERR_INVALID_ARG
-    # too many tokens for 32-bit packed indices
+    # too many tokens for 32-bit byte offsets within a head (N + 256 >= 2^24)
     s = S(40000, 1369, 5, 1, 128)
     assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
+    s = S(12211, 1369, 5, 1, 128)    # 16,777,914 tokens
+    assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.ERR_UNSUPPORTED
+    s = S(12210, 1369, 5, 1, 128)    # 16,776,540 tokens: largest accepted frame count here
+    assert lib.bsga_num_blocks(ctypes.byref(s.c()), ctypes.byref(out)) == bsga.OK
 
 
 def test_keep_count_rejects_bad_rho():
