@@ -1,5 +1,6 @@
-"""Seeded sweep over random small layer shapes, each checked against the
-oracle end to end: frames 1-8, patch grids 2x2 to 32x32, 0-7 special tokens
+"""Seeded sweep over random small layer shapes (16 by default; the
+environment variable BSGA_RANDOM_SHAPES sets another count), each checked
+against the oracle end to end: frames 1-8, patch grids 2x2 to 32x32, 0-7 special tokens
 per frame, 1-3 heads, b = 64 or 128, head kinds diffuse / planted
 correspondences / position code, rho and tau drawn per shape (including
 tau = 0 and tau = 1), plus two shapes whose rows are all empty.
@@ -58,7 +59,8 @@ def _shapes(n=16, seed=2024):
     return out
 
 
-SHAPES = _shapes()
+# BSGA_RANDOM_SHAPES=n widens the sweep to n random shapes (default 16)
+SHAPES = _shapes(int(__import__("os").environ.get("BSGA_RANDOM_SHAPES", "16")))
 
 
 @pytest.fixture(scope="module")
