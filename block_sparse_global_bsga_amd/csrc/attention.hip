@@ -537,8 +537,9 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Rows that kSparseTail split into pieces: workgroup (XCD x and tail row t,
-// group g of 4 query rows) merges the row's float32 partials by
+// Rows that kSparseTail split into pieces: workgroup (XCD x and tail row
+// t < tmax, the largest leftover of any XCD; group g of 4 query rows) merges
+// the row's float32 partials by
 // log-sum-exp and writes O and LSE of those queries; thread T owns dimension
 // T % 64 of query 4 g + T / 64.  Many small workgroups keep the partials'
 // reads in flight (the merge is memory-bound).
@@ -547,9 +548,9 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          uint16_t* __restrict__ o,
                                                          float* __restrict__ lse, Dims d,
                                                          int rows, int rows_per_xcd, int m,
-                                                         int pieces) {
+                                                         int pieces, int tmax) {
   constexpr int QT = 128;
-  const int x = blockIdx.x / m, t = blockIdx.x % m;
+  const int x = blockIdx.x / tmax, t = blockIdx.x % tmax;
   const int r0 = x * rows_per_xcd;
   const int n_x = min(rows, r0 + rows_per_xcd) - r0;
   if (n_x <= 0) return;
@@ -678,7 +679,7 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
 // unit; 96 when the device cannot be queried) and the compact slot count of the
 // pieces of every XCD's last, partial round.
 struct TailPlan {
-  int m, rows, rows_per_xcd, pieces, slots, grid;
+  int m, rows, rows_per_xcd, pieces, slots, grid, max_rem;
 };
 static TailPlan tail_plan(const Dims& d) {
   TailPlan p;
@@ -700,6 +701,7 @@ static TailPlan tail_plan(const Dims& d) {
     const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
     if (n_x > 0) max_rem = max(max_rem, n_x % p.m);
   }
+  p.max_rem = max_rem;
   if (max_rem == 0 || p.m / max_rem < 2) return p;
   p.pieces = min(kMaxTailPieces, p.m / max_rem);
   for (int x = 0; x < kXcds; ++x) {
@@ -740,9 +742,8 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       attn_kernel<128, 128, kSparseTail, 3><<<kXcds * p.grid, 256, 0, st>>>(a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      tail_merge_kernel<<<dim3(kXcds * p.m, 128 / 4), 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d,
-                                                                     p.rows, p.rows_per_xcd, p.m,
-                                                                     p.pieces);
+      tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
+          a.part_o, a.part_ml, o, lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem);
       return hipGetLastError();
     }
   }
