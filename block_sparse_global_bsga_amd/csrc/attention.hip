@@ -124,7 +124,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   __shared__ u32x4 smem[2 * KCH];   // the K tile, then the V^T tile
 
   const Dims& d = a.d;
-  const int T = threadIdx.x, lane = T & 63;
+  const int T = lid_x(), lane = T & 63;
   const int w = __builtin_amdgcn_readfirstlane(T >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   {
     int item;
     if constexpr (MODE == kSparseTail) {
-      const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+      const int x = wg_x() % kXcds, j = wg_x() / kXcds;
       const int r0 = x * a.rows_per_xcd;
       const int n_x = min(a.n_items, r0 + a.rows_per_xcd) - r0;
       if (n_x <= 0) return;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         piece_slot = ((size_t)x * (a.rows_per_xcd % a.tail_m) + t) * a.tail_pieces + piece;
       }
     } else {
-      item = xcd_item(blockIdx.x, a.n_items);
+      item = xcd_item(wg_x(), a.n_items);
       if (item < 0) return;
     }
     if constexpr (MODE == kSparseFused || MODE == kSparseTail) {
@@ -515,8 +515,8 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
                                                              uint16_t* __restrict__ o,
                                                              float* __restrict__ lse, Dims d,
                                                              int nsplit) {
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int item = wg_x() * 4 + (lid_x() >> 6);
+  const int lane = lid_x() & 63;
   if (item >= d.H * d.ns) return;
   const int h = item / d.ns, s = item - h * d.ns;
   const size_t base = ((size_t)h * d.ns_pad + s) * nsplit;
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          int rows, int rows_per_xcd, int m,
                                                          int pieces, int tmax) {
   constexpr int QT = 128;
-  const int x = blockIdx.x / tmax, t = blockIdx.x % tmax;
+  const int x = wg_x() / tmax, t = wg_x() % tmax;
   const int r0 = x * rows_per_xcd;
   const int n_x = min(rows, r0 + rows_per_xcd) - r0;
   if (n_x <= 0) return;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
   if (t >= rem) return;
   const int item = r0 + full + t;
   const size_t slot0 = ((size_t)x * (rows_per_xcd % m) + t) * pieces;
-  const int T = threadIdx.x, dim = T & 63, qr = 4 * blockIdx.y + (T >> 6);
+  const int T = lid_x(), dim = T & 63, qr = 4 * wg_y() + (T >> 6);
   float mi[kMaxTailPieces], li[kMaxTailPieces], oi[kMaxTailPieces];
   float M = -INFINITY;
 #pragma unroll
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
                                                    uint4* __restrict__ kp,
                                                    uint4* __restrict__ vt, Dims d) {
   __shared__ uint16_t sv[64][66];
-  const int kp0 = blockIdx.x * 64, h = blockIdx.y, T = threadIdx.x;
+  const int kp0 = wg_x() * 64, h = wg_y(), T = lid_x();
   const size_t src_head = (size_t)h * d.n * 8;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint4* __restrict__
                                                        uint4* __restrict__ rows,
                                                        uint4* __restrict__ cols, Dims d) {
   __shared__ uint16_t sv[64][66];
-  const int kp0 = blockIdx.x * 64, h = blockIdx.y, T = threadIdx.x;
+  const int kp0 = wg_x() * 64, h = wg_y(), T = lid_x();
   const size_t src_head = (size_t)h * d.n * 8;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restri
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ lse2,
                                                            float* __restrict__ dd, Dims d) {
-  const int h = blockIdx.y, T = threadIdx.x, ch = T & 7;
-  const int kp = blockIdx.x * 32 + (T >> 3);  // 32 rows per workgroup, 8 lanes per row
+  const int h = wg_y(), T = lid_x(), ch = T & 7;
+  const int kp = wg_x() * 32 + (T >> 3);  // 32 rows per workgroup, 8 lanes per row
   const int tok = packed_token(kp, d);
   float s = 0.f;
   if (tok >= 0) {
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void csr_t_count_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ col_idx,
                                                           Dims d, int32_t* __restrict__ count) {
   __shared__ int red[4];
-  const int j = blockIdx.x, h = blockIdx.y, T = threadIdx.x;
+  const int j = wg_x(), h = wg_y(), T = lid_x();
   int c = 0;
   for (int i = T; i < d.B; i += 256) {
     const int r = h * d.B + i;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void csr_t_fill_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ t_ptr, Dims d,
                                                          int32_t* __restrict__ t_list) {
   __shared__ int wave_tot[4];
-  const int j = blockIdx.x, h = blockIdx.y, T = threadIdx.x;
+  const int j = wg_x(), h = wg_y(), T = lid_x();
   const int per = (d.B + 255) / 256;
   const int lo = min(d.B, T * per), hi = min(d.B, lo + per);
   int local = 0;
@@ -282,9 +282,9 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
   constexpr uint32_t kTile = KCH * 16;   // bytes of one tile
   __shared__ u32x4 smem[2 * 3 * KCH];  // slot s: K rows, V rows, K^T
   const Dims& d = a.d;
-  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, a.n_items));
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(wg_x(), a.n_items));
   if (item < 0) return;
-  const int T = threadIdx.x, lane = T & 63;
+  const int T = lid_x(), lane = T & 63;
   const int w = __builtin_amdgcn_readfirstlane(T >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int q_tiles = d.B + d.ns_pad / QT;
@@ -459,9 +459,9 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
   __shared__ u32x4 smem[2 * 4 * QCH];
   __shared__ float stats[2][2][QT];
   const Dims& d = a.d;
-  const int item = __builtin_amdgcn_readfirstlane(xcd_item(blockIdx.x, a.n_items));
+  const int item = __builtin_amdgcn_readfirstlane(xcd_item(wg_x(), a.n_items));
   if (item < 0) return;
-  const int T = threadIdx.x, lane = T & 63;
+  const int T = lid_x(), lane = T & 63;
   const int w = __builtin_amdgcn_readfirstlane(T >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int k_tiles = d.B + d.ns_pad / KT;

@@ -36,13 +36,17 @@ inline FastDiv make_fastdiv(uint32_t d) {
 }
 
 __host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t t = __umulhi(n, f.m);
-#else
-  uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
-#endif
+  const uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);  // v_mul_hi_u32 on the device
   return (uint32_t)(((uint64_t)t + n) >> f.l);
 }
+
+// Workgroup and work-item ids straight from the hardware registers.  The
+// attention and backward kernels are compiled without IEEE mode (their max
+// chains never see NaNs), which keeps the device library's id functions from
+// being inlined into them; the builtins need no call.
+__device__ inline int wg_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ inline int wg_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ inline int lid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
 
 // Layer geometry.  "Packed order" lists keys (and queries) as the N_p patch
 // tokens in patch order, zero padding up to np_pad, then the N_s special
