@@ -509,7 +509,9 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
 
 // ---------------------------------------------------------------------------
 // Split-K reduction for the special queries: one wave per (head, special
-// token), one lane per dimension.
+// token), one lane per dimension.  The splits' (max, sum) pairs are read one
+// per lane, 64 at a time, and broadcast; the partial rows are then summed in
+// split order with their loads independent of the running sums.
 __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              uint16_t* __restrict__ o,
@@ -521,14 +523,27 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
   const int h = item / d.ns, s = item - h * d.ns;
   const size_t base = ((size_t)h * d.ns_pad + s) * nsplit;
   float M = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, part_ml[(base + c) * 2]);
+  for (int c = lane; c < nsplit; c += 64) M = fmaxf(M, part_ml[(base + c) * 2]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   float L = 0.f, acc = 0.f;
-  for (int c = 0; c < nsplit; ++c) {
-    const float mc = part_ml[(base + c) * 2];
-    if (mc == -INFINITY) continue;
-    const float wgt = fast_exp2((mc - M) * kScaleLog2);
-    L += wgt * part_ml[(base + c) * 2 + 1];
-    acc += wgt * part_o[(base + c) * kHeadDim + lane];
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
+    const int c = c0 + lane, cn = min(64, nsplit - c0);
+    float wgt = 0.f, lc = 0.f;
+    if (c < nsplit) {
+      const float mc = part_ml[(base + c) * 2];
+      lc = part_ml[(base + c) * 2 + 1];
+      // a split without any valid key carries max -inf and adds nothing
+      wgt = mc == -INFINITY ? 0.f : fast_exp2((mc - M) * kScaleLog2);
+    }
+    const float* po = part_o + (base + c0) * kHeadDim + lane;
+#pragma unroll 8
+    for (int j = 0; j < cn; ++j) {
+      const float wj = __shfl(wgt, j), lj = __shfl(lc, j);
+      const float oj = po[(size_t)j * kHeadDim];
+      L += wj * lj;
+      acc += wj * oj;
+    }
   }
   const int tok = special_token(s, d);
   o[((size_t)h * d.n + tok) * kHeadDim + lane] =
@@ -681,14 +696,20 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
 struct TailPlan {
   int m, rows, rows_per_xcd, pieces, slots, grid, max_rem;
 };
-static TailPlan tail_plan(const Dims& d) {
-  TailPlan p;
+// Workgroup slots of the current device for 128 x 128 workgroups: three per
+// compute unit (768 when the device cannot be queried).
+static int device_slots() {
   int dev = 0, cus = 0;
-  p.m = 96;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       cus >= kXcds / 2)
-    p.m = 3 * cus / kXcds;
+    return 3 * cus;
+  return 768;
+}
+
+static TailPlan tail_plan(const Dims& d) {
+  TailPlan p;
+  p.m = device_slots() / kXcds;
   p.rows = d.H * d.B;
   p.rows_per_xcd = (p.rows + kXcds - 1) / kXcds;
   p.pieces = 0;
@@ -753,14 +774,26 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
 struct SplitPlan {
   int q_tiles, nsplit, tps;
 };
+// Key ranges of the special queries: the split count that minimises
+// rounds of workgroups x (tiles per workgroup + one tile's worth of prologue
+// and partial store), fewest splits on ties (less to reduce).
 static SplitPlan special_plan(const Dims& d) {
   SplitPlan p;
   p.q_tiles = d.ns_pad / 128;
   const int nt = d.ntot_pad / 128;
-  int want = 1024 / max(1, d.H * p.q_tiles);
-  want = max(1, min(want, nt));
-  p.tps = (nt + want - 1) / want;
-  p.nsplit = (nt + p.tps - 1) / p.tps;
+  const long slots = device_slots(), per_split = (long)d.H * p.q_tiles;
+  p.tps = nt;
+  p.nsplit = 1;
+  long best = -1;
+  for (int want = 1; want <= min(nt, 1024); ++want) {
+    const int tps = (nt + want - 1) / want, ns = (nt + tps - 1) / tps;
+    const long cost = (per_split * ns + slots - 1) / slots * (tps + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      p.tps = tps;
+      p.nsplit = ns;
+    }
+  }
   return p;
 }
 
