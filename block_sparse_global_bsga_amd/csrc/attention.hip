@@ -715,16 +715,32 @@ static TailPlan tail_plan(const Dims& d) {
   p.pieces = 0;
   p.slots = 0;
   p.grid = 0;
-  // as many pieces per row as let the largest last round fit in one round
-  // of slots; a last round more than half full is not split
+  // Pieces per leftover row.  A largest leftover of at most half a round:
+  // as many pieces as let them all run in one round of slots.  A fuller last
+  // round: the count p <= kMaxTailPieces whose pieces, in ceil(max_rem p /
+  // m) rounds of 1/p of a row each, finish first (plus about one key tile
+  // of the row, 1 / (B + 1) of it, per piece for its prologue and partial
+  // store), if that beats 0.8 of a row; else the round runs unsplit.
   int max_rem = 0;
   for (int x = 0; x < kXcds; ++x) {
     const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
     if (n_x > 0) max_rem = max(max_rem, n_x % p.m);
   }
   p.max_rem = max_rem;
-  if (max_rem == 0 || p.m / max_rem < 2) return p;
-  p.pieces = min(kMaxTailPieces, p.m / max_rem);
+  if (max_rem == 0) return p;
+  if (p.m / max_rem >= 2) {
+    p.pieces = min(kMaxTailPieces, p.m / max_rem);
+  } else {
+    double best = 0.8;
+    for (int pc = 2; pc <= kMaxTailPieces; ++pc) {
+      const double cost = (double)((max_rem * pc + p.m - 1) / p.m) / pc + (double)pc / (d.B + 1);
+      if (cost < best) {
+        best = cost;
+        p.pieces = pc;
+      }
+    }
+    if (p.pieces == 0) return p;
+  }
   for (int x = 0; x < kXcds; ++x) {
     const int n_x = min(p.rows, (x + 1) * p.rows_per_xcd) - x * p.rows_per_xcd;
     if (n_x <= 0) break;

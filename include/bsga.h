@@ -293,13 +293,17 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
  *     merge in bsga_special_dense, without the intermediate bf16 rounding).
  *     Optional workspace (NULL, or bsga_workspace_bytes(
- *     BSGA_OP_PATCH_ROWS_PACKED) bytes: 0 for b = 64, and 0 when the last
- *     round of workgroups is more than half full): with it, at b = 128 the
- *     query blocks left for the last, partial round of workgroups are split
- *     into pieces of consecutive key tiles (as many per block as let them
- *     all run at once) whose float32 partials are merged by log-sum-exp
+ *     BSGA_OP_PATCH_ROWS_PACKED) bytes: 0 for b = 64, and 0 when splitting
+ *     would not shorten the last round): with it, at b = 128 the query
+ *     blocks left for the last, partial round of workgroups are split into
+ *     pieces of consecutive key tiles (as many per block as let them all run
+ *     at once when that round is at most half full; for a fuller round the
+ *     count, at most 16, whose pieces finish first, if that is under 0.8 of
+ *     a block's time) whose float32 partials are merged by log-sum-exp
  *     afterwards, which balances that round; the result is the same softmax
- *     (it may differ from the unsplit rows in the last bit);
+ *     (it may differ from the unsplit rows in the last bit).  The plan uses
+ *     the compute-unit count of the current device: size and use the
+ *     workspace with the same device current;
  *   bsga_special_rows_packed: every special query attends to all N tokens
  *     (split over key ranges, partial results combined by log-sum-exp in a
  *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and

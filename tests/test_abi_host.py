@@ -58,18 +58,31 @@ def test_keep_count_matches_oracle_definition():
         assert bsga.keep_count(B, rho) == O.keep_count(B, rho)
 
 
-def tail_bytes(rows, m=96, xcds=8, max_pieces=16):
-    """Workspace of the split last round, as the plan defines it: rows dealt
-    to XCDs in equal contiguous ranges, m slots per XCD, as many pieces per
-    leftover row as fit one round (at most max_pieces; none when the largest
-    leftover exceeds half a round)."""
+def tail_pieces(max_rem, blocks, m=96, max_pieces=16):
+    """Pieces per leftover row, as the plan defines them: for a largest
+    leftover of at most half a round, as many as fit one round (at most
+    max_pieces); for a fuller round the count whose ceil(max_rem p / m)
+    rounds of 1/p of a row, plus 1 / (blocks + 1) of a row per piece, finish
+    first, if under 0.8 of a row; else none."""
+    if max_rem == 0:
+        return 0
+    if m // max_rem >= 2:
+        return min(max_pieces, m // max_rem)
+    best, pieces = 0.8, 0
+    for p in range(2, max_pieces + 1):
+        cost = (-(-max_rem * p // m)) / p + p / (blocks + 1)
+        if cost < best:
+            best, pieces = cost, p
+    return pieces
+
+
+def tail_bytes(rows, blocks, m=96, xcds=8, max_pieces=16):
+    """Workspace of the split last round: rows dealt to XCDs in equal
+    contiguous ranges, m slots per XCD, tail_pieces pieces per leftover row."""
     per = -(-rows // xcds)
     rems = [(min(rows, (x + 1) * per) - x * per) % m for x in range(xcds)
             if min(rows, (x + 1) * per) > x * per]
-    if max(rems) == 0 or m // max(rems) < 2:
-        return 0
-    pieces = min(max_pieces, m // max(rems))
-    return sum(rems) * pieces * 128 * 66 * 4
+    return sum(rems) * tail_pieces(max(rems), blocks, m, max_pieces) * 128 * 66 * 4
 
 
 def test_capacity_and_workspace_sizes():
@@ -89,20 +102,28 @@ def test_capacity_and_workspace_sizes():
     # assumes 96 workgroup slots per XCD: 5488 rows are 686 per XCD, 14 of
     # them in the last round, split into 96 // 14 = 6 pieces each
     tail = bsga.workspace_bytes(shape, bsga.OP_PATCH_ROWS_PACKED)
-    assert tail_bytes(5488) == 8 * 14 * 6 * 128 * 66 * 4
-    assert tail_bytes(5488) <= tail <= tail_bytes(5488) + 512
+    assert tail_bytes(5488, 343) == 8 * 14 * 6 * 128 * 66 * 4
+    assert tail_bytes(5488, 343) <= tail <= tail_bytes(5488, 343) + 512
     assert bsga.workspace_bytes(shape, bsga.OP_LAYER) >= tail
     assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) <= 1
-    # 400 rows: 50 per XCD, a last round more than half full is not split
-    assert bsga.workspace_bytes(S(1, 3200, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    # 400 rows (16 heads x 25 blocks): 50 per XCD, more than half a round: 3
+    # pieces each, in two rounds of a third of a row
+    assert tail_pieces(50, 25) == 3 and tail_bytes(400, 25) == 8 * 50 * 3 * 128 * 66 * 4
+    assert tail_bytes(400, 25) <= bsga.workspace_bytes(S(1, 3200, 5, 16, 128),
+                                                   bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(400, 25) + 512
+    # the 100- and 200-frame layers: 64 and 56 of 96 slots in the last round
+    assert tail_pieces(64, 608) == 3 and tail_pieces(56, 2140) == 12
+    # 720 rows (16 x 45): 90 per XCD, no piece count shortens the round
+    assert tail_pieces(90, 45) == 0
+    assert bsga.workspace_bytes(S(1, 5760, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) <= 1
     # 8 rows: one per XCD, split into the most pieces (16)
-    assert tail_bytes(8) == 8 * 1 * 16 * 128 * 66 * 4
-    assert tail_bytes(8) <= bsga.workspace_bytes(S(1, 1024, 5, 1, 128),
-                                                 bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(8) + 512
+    assert tail_bytes(8, 8) == 8 * 1 * 16 * 128 * 66 * 4
+    assert tail_bytes(8, 8) <= bsga.workspace_bytes(S(1, 1024, 5, 1, 128),
+                                                 bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(8, 8) + 512
     # 64 rows: 8 per XCD, 96 // 8 = 12 pieces
-    assert tail_bytes(64) == 8 * 8 * 12 * 128 * 66 * 4
-    assert tail_bytes(64) <= bsga.workspace_bytes(S(1, 1024, 5, 8, 128),
-                                                  bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(64) + 512
+    assert tail_bytes(64, 8) == 8 * 8 * 12 * 128 * 66 * 4
+    assert tail_bytes(64, 8) <= bsga.workspace_bytes(S(1, 1024, 5, 8, 128),
+                                                  bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(64, 8) + 512
     assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PATCH_ROWS_PACKED + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 

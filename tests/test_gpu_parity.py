@@ -41,6 +41,8 @@ def _cases():
                                                       kind="corr"), None),
         "position-b128": (lambda: synth.random_layer(4, 12, 12, 2, 128, seed=14, kind="pos"), None),
         "single-block": (lambda: synth.random_layer(1, 8, 8, 1, 128, seed=15), None),
+        # 400 query blocks: 50 per XCD left for a last round of 96 slots
+        "over-half-b128": (lambda: synth.random_layer(1, 40, 80, 16, 128, seed=21), None),
     }
 
 
@@ -424,15 +426,17 @@ def test_end_to_end_mask_vs_oracle_pipeline(lib):
             f"(nnz gpu {rp[-1]}, oracle {orp[-1]})")
 
 
-def _split_rows(rows, m, xcds=8):
+def _split_rows(rows, blocks, m, xcds=8):
     """Rows (head-major query blocks) that the patch-row call at b = 128 runs
     as key-range pieces: those of each XCD's last, partial round of m
-    workgroup slots (rows are dealt to XCDs in equal contiguous ranges)."""
+    workgroup slots (rows are dealt to XCDs in equal contiguous ranges),
+    unless no piece count shortens that round."""
+    from test_abi_host import tail_pieces
     per = -(-rows // xcds)
     rems = [(min(rows, (x + 1) * per) - x * per) % m for x in range(xcds)
             if min(rows, (x + 1) * per) > x * per]
-    if max(rems) == 0 or m // max(rems) < 2:
-        return []  # a last round more than half full is not split
+    if tail_pieces(max(rems), blocks, m) == 0:
+        return []
     out = []
     for x in range(xcds):
         r0 = x * per
@@ -444,7 +448,7 @@ def _split_rows(rows, m, xcds=8):
     return out
 
 
-@pytest.mark.parametrize("name", ["vggt-32f", "ragged-b128"])
+@pytest.mark.parametrize("name", ["vggt-32f", "ragged-b128", "over-half-b128"])
 def test_patch_rows_tail_pieces(lib, name):
     """bsga_patch_rows_packed with its workspace splits the rows of the last,
     partial round into key-range pieces and merges them: those rows (every
@@ -467,7 +471,7 @@ def test_patch_rows_tail_pieces(lib, name):
     torch.cuda.synchronize()
     B = lib.num_blocks(shape)
     m = 3 * torch.cuda.get_device_properties(0).multi_processor_count // 8
-    split = _split_rows(cfg.heads * B, m)
+    split = _split_rows(cfg.heads * B, B, m)
     say(f"[tail pieces] {name}: {len(split)} of {cfg.heads * B} query blocks split, {m} slots/XCD")
     assert split, "the shape should leave a partial last round"
     rp = row_ptr.cpu().numpy().astype(np.int64)
@@ -500,18 +504,18 @@ def test_patch_rows_tail_pieces(lib, name):
 
 
 def test_patch_rows_unsplit_when_last_round_large(lib):
-    """400 query blocks (16 heads x 25) leave 50 per XCD for the last round of
-    96 slots: more than half a round, so the plan splits nothing, the
+    """720 query blocks (16 heads x 45) leave 90 per XCD for the last round of
+    96 slots: no piece count shortens it, so the plan splits nothing, the
     workspace is empty, and the call with a workspace is byte-identical to
     the one without."""
     import torch
     from gpu_helpers import layer_shape, say
-    x = synth.random_layer(1, 40, 80, 16, 128, seed=21)
+    x = synth.random_layer(1, 72, 80, 16, 128, seed=21)
     cfg = x.cfg
     shape = layer_shape(cfg)
     B = lib.num_blocks(shape)
     m = 3 * torch.cuda.get_device_properties(0).multi_processor_count // 8
-    if _split_rows(cfg.heads * B, m):
+    if _split_rows(cfg.heads * B, B, m):
         pytest.skip(f"{m} slots per XCD split this shape")
     assert lib.workspace_bytes(shape, lib.OP_PATCH_ROWS_PACKED) <= 1
     q, k, v = _upload(x)
