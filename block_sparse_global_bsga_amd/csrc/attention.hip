@@ -304,6 +304,10 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   f32x16 o0, o1;
   float m_run, l_run;
   const int qrow = qp0 + 32 * w + l32;
+  // kSpecialSplit: a wave whose 32 rows all lie past the last special token
+  // skips its scores and P V products; it still issues its share of every
+  // tile load and meets every barrier
+  const bool idle = MODE == kSpecialSplit && qp0 - d.np_pad + 32 * w >= d.ns;
 
   // Rare block: masking of a partial tile, exact max, rescaling.  Score r of
   // sub-tile t is key 32 t + pi(8 (r / 4) + 4 hh + r % 4) = kc + 8 hh with
@@ -370,19 +374,21 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       issue_v(kp_n);
       const int raw_after = tile_raw(n + 2);
       f32x16 s[NS];
-      float mx = -INFINITY;
+      if (!idle) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
+        for (int t = 0; t < NS; ++t) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kadr[m] + t * kSubK), qop[m],
-                                                         m == 0 ? f32x16{} : s[t], 0, 0, 0);
-        // a plain chain: the backend folds it into one v_max3 per two scores
+          for (int m = 0; m < 4; ++m)
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kadr[m] + t * kSubK), qop[m],
+                                                           m == 0 ? f32x16{} : s[t], 0, 0, 0);
+          // a plain chain: the backend folds it into one v_max3 per two scores
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+        }
+        const int valid = tile_valid(kp_n);
+        if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
       }
-      const int valid = tile_valid(kp_n);
-      if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
       // V^T(n) has landed and every wave is done with K(n): K(n+1) fills the
       // K slot while tile n is exponentiated and multiplied by V^T
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       // MFMAs) from starving the VALU
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
+      for (int t = 0; t < (idle ? 0 : NS); ++t) {
         // the sub-tile's V^T operands are read first and may not be sunk, so
         // the LDS latency hides behind the exponentials
         bf16x8 va[2], vb[2];
@@ -537,12 +543,17 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
       wgt = mc == -INFINITY ? 0.f : fast_exp2((mc - M) * kScaleLog2);
     }
     const float* po = part_o + (base + c0) * kHeadDim + lane;
-#pragma unroll 8
-    for (int j = 0; j < cn; ++j) {
-      const float wj = __shfl(wgt, j), lj = __shfl(lc, j);
-      const float oj = po[(size_t)j * kHeadDim];
-      L += wj * lj;
-      acc += wj * oj;
+    // eight splits per step; past the last split the weight (lane >= cn) is
+    // 0 and the load repeats the last split's row, so the sums are unchanged
+    for (int j0 = 0; j0 < cn; j0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const float wj = __shfl(wgt, j), lj = __shfl(lc, j);
+        const float oj = po[(size_t)min(j, cn - 1) * kHeadDim];
+        L += wj * lj;
+        acc += wj * oj;
+      }
     }
   }
   const int tok = special_token(s, d);
