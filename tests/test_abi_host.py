@@ -128,6 +128,38 @@ def test_capacity_and_workspace_sizes():
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 
 
+def special_splits(heads, special_tiles, key_tiles, slots=768):
+    """Key ranges of the special rows, as the plan defines them: the count
+    minimising rounds of workgroups (heads x special query tiles x ranges
+    over `slots`) times (tiles per range + 1), fewest ranges on ties."""
+    best = None
+    for want in range(1, min(key_tiles, 1024) + 1):
+        tps = -(-key_tiles // want)
+        ns = -(-key_tiles // tps)
+        cost = -(-heads * special_tiles * ns // slots) * (tps + 1)
+        if best is None or cost < best[0]:
+            best = (cost, ns)
+    return best[1]
+
+
+def test_special_rows_workspace():
+    """The special rows' split-K workspace holds float32 partial rows (64
+    values, max and sum) for every (head, padded special row, key range)."""
+    def expect(shape, ns):
+        slots = shape.heads * (-(-shape.frames * shape.special_per_frame // 128) * 128) * ns
+        return ((slots * 64 * 4 + 255) & ~255) + slots * 2 * 4
+    # 32 frames: 16 heads x 2 special query tiles; 343 + 2 key tiles split
+    # into 23 ranges of 15 (736 workgroups, one round of 768 slots)
+    c3 = S(32, 1369, 5, 16, 128)
+    assert special_splits(16, 2, 345) == 23
+    assert bsga.workspace_bytes(c3, bsga.OP_SPECIAL_DENSE_PACKED) == expect(c3, 23)
+    # one head, 8 frames of 32 x 32 patches: 64 + 1 key tiles, one range each
+    one = S(8, 1024, 5, 1, 128)
+    assert special_splits(1, 1, 65) == 65
+    assert bsga.workspace_bytes(one, bsga.OP_SPECIAL_DENSE_PACKED) == expect(one, 65)
+    assert bsga.workspace_bytes(S(4, 256, 0, 2, 64), bsga.OP_SPECIAL_DENSE_PACKED) == 0
+
+
 def test_probe_select_validation():
     """Argument checks of bsga_probe_select run before any launch (no GPU)."""
     shape = S(2, 16, 5, 2, 64)

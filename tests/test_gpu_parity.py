@@ -43,6 +43,9 @@ def _cases():
         "single-block": (lambda: synth.random_layer(1, 8, 8, 1, 128, seed=15), None),
         # 400 query blocks: 50 per XCD left for a last round of 96 slots
         "over-half-b128": (lambda: synth.random_layer(1, 40, 80, 16, 128, seed=21), None),
+        # one head, 64 + 1 key tiles: the special rows split into 65 key
+        # ranges, more than one 64-lane pass of the split-K reduce
+        "special-65-splits": (lambda: synth.random_layer(8, 32, 32, 1, 128, seed=22), None),
     }
 
 
