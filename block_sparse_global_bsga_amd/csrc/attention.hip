@@ -70,8 +70,13 @@ namespace bsga {
 //                whole rows: the in-order dispatch then spreads that round
 //                over every slot, and concurrent pieces read the same key range
 //                of consecutive rows; tail_merge_kernel combines the pieces
+// kSparsePrecise: kSparseFused for the rows of at most kPreciseKeys keys
+//                only (every other workgroup returns at once), with P fed to
+//                the P V product as bf16 hi + lo; launched after the patch
+//                rows, it rewrites those rows
 enum Mode {
-  kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5
+  kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5,
+  kSparsePrecise = 6
 };
 
 // most pieces per row of the last round (kSparseTail)
@@ -106,6 +111,13 @@ constexpr float kLazySlack = 64.f;
 
 // Fourth word of a raw buffer resource (byte addressing, 32-bit data format)
 constexpr int kBufWord3 = 0x00020000;
+
+// Patch rows with at most this many keys in all (kept blocks and special
+// tiles) feed P to the P V product as a bf16 pair hi + lo (16 significant
+// bits) instead of one bf16: with few keys each weight carries a large share
+// of the output, and the single rounding (2^-9 relative) would show in it.
+// Such rows are short, so the extra products cost the layer next to nothing.
+constexpr int kPreciseKeys = 2048;
 
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       item = xcd_item(wg_x(), a.n_items);
       if (item < 0) return;
     }
-    if constexpr (MODE == kSparseFused || MODE == kSparseTail) {
+    if constexpr (MODE == kSparseFused || MODE == kSparseTail || MODE == kSparsePrecise) {
       h = item / d.B;
       qp0 = (item - h * d.B) * QT;
       const int r0 = a.row_ptr[item];
@@ -191,12 +203,16 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
     tile0 = __builtin_amdgcn_readfirstlane(tile0);
   }
+  // (uniform per workgroup, before any LDS use or barrier)
+  if constexpr (MODE == kSparsePrecise) {
+    if (nt * KT > kPreciseKeys) return;
+  }
   // Position of tile n, in two steps so that the global load of a CSR entry
   // can be issued long before its value is consumed: tile_raw(n) loads the
   // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
   // it into the tile's first packed key.  Kept block j of the row covers tiles
   // j TPB .. j TPB + TPB - 1.
-  constexpr bool kCsr = MODE == kSparseFused || MODE == kSparseTail;
+  constexpr bool kCsr = MODE == kSparseFused || MODE == kSparseTail || MODE == kSparsePrecise;
   auto tile_raw = [&](int n) -> int {
     if constexpr (kCsr) {
       return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0;
@@ -345,7 +361,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   // beside the P V products of the previous one).  CSR entries run two tiles
   // ahead: the entry of tile n+2 is loaded during iteration n and consumed
   // after that iteration's waits.
-  auto run_tiles = [&](int n0, int n1) {
+  auto run_tiles = [&](int n0, int n1, auto precise_tag) {
+    constexpr bool kPrecise = decltype(precise_tag)::value;
     {
       const int qtok = packed_token(qrow, d);
       const u32x4* src =
@@ -421,6 +438,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
           const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
           o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pb, o0, 0, 0, 0);
           o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pb, o1, 0, 0, 0);
+          if constexpr (kPrecise) {
+            f32x8 r8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r8[e] = e8[e] - (float)pb[e];
+            const bf16x8 pl = __builtin_convertvector(r8, bf16x8);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pl, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pl, o1, 0, 0, 0);
+          }
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -491,17 +516,20 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     if (hh == 0) *lrow = lse_out;
   };
 
-  if constexpr (MODE == kSparseTail) {
+  if constexpr (MODE == kSparsePrecise) {
+    run_tiles(0, nt, std::true_type{});
+    store_rows();
+  } else if constexpr (MODE == kSparseTail) {
     if (piece < 0) {
-      run_tiles(0, nt);
+      run_tiles(0, nt, std::false_type{});
       store_rows();
     } else {
-      run_tiles(nt * piece / a.tail_pieces, nt * (piece + 1) / a.tail_pieces);
+      run_tiles(nt * piece / a.tail_pieces, nt * (piece + 1) / a.tail_pieces, std::false_type{});
       const size_t row = piece_slot * QT + 32 * w + l32;
       store_partial(a.part_o + row * kHeadDim, a.part_ml + row * 2, false);
     }
   } else {
-    run_tiles(0, nt);
+    run_tiles(0, nt, std::false_type{});
     if constexpr (MODE == kSpecialSplit) {
       const int sq = qrow - d.np_pad;
       const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
@@ -676,6 +704,12 @@ template <int MODE>
 static hipError_t run_attn_b(const Dims& d, const AttnArgs& a, hipStream_t st) {
   return d.b == 64 ? run_attn<64, 64, MODE>(a, st) : run_attn<128, 128, MODE>(a, st);
 }
+// the short rows again with P as bf16 hi + lo, at two waves per SIMD (room
+// for the extra operands without spilling)
+static hipError_t run_precise(const Dims& d, const AttnArgs& a, hipStream_t st) {
+  return d.b == 64 ? run_attn<64, 64, kSparsePrecise, 2>(a, st)
+                   : run_attn<128, 128, kSparsePrecise, 2>(a, st);
+}
 
 
 static AttnArgs base_args(const Dims& d, const uint16_t* q, const uint16_t* kp,
@@ -698,7 +732,8 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
   a.patch_only = 1;
-  return run_attn_b<kSparseFused>(d, a, st);
+  const hipError_t e = run_attn_b<kSparseFused>(d, a, st);
+  return e != hipSuccess ? e : run_precise(d, a, st);
 }
 
 // kSparseTail plan: slots per XCD (three 128 x 128 workgroups per compute
@@ -792,10 +827,12 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       if (e != hipSuccess) return e;
       tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
           a.part_o, a.part_ml, o, lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem);
-      return hipGetLastError();
+      e = hipGetLastError();
+      return e != hipSuccess ? e : run_precise(d, a, st);
     }
   }
-  return run_attn_b<kSparseFused>(d, a, st);
+  const hipError_t e = run_attn_b<kSparseFused>(d, a, st);
+  return e != hipSuccess ? e : run_precise(d, a, st);
 }
 
 struct SplitPlan {
