@@ -3,7 +3,8 @@ environment variable BSGA_RANDOM_SHAPES sets another count), each checked
 against the oracle end to end: frames 1-8, patch grids 2x2 to 32x32, 0-7 special tokens
 per frame, 1-3 heads, b = 64 or 128, head kinds diffuse / planted
 correspondences / position code, rho and tau drawn per shape (including
-tau = 0 and tau = 1), plus two shapes whose rows are all empty.
+tau = 0 and tau = 1), plus two shapes whose rows are all empty and two
+draws of the wider sweep whose rows keep few keys.
 
 Per shape, through the C ABI:
 * bsga_layer's CSR equals the oracle's selection of the GPU's own float32
@@ -56,6 +57,13 @@ def _shapes(n=16, seed=2024):
     # patch has any key; with them, only the special keys remain
     out.append((n, 3, 17, 9, 0, 2, 64, "corr", 0.99, 0.0))
     out.append((n + 1, 3, 17, 9, 5, 2, 64, "corr", 0.99, 0.0))
+    # two draws of the wider sweep (same index, so the same seeds) whose rows
+    # keep few keys: with P rounded once to bf16 their outputs missed the bar
+    # (2.06e-2 and 2.05e-2 of rms(O_dense)); rows this short take P as hi + lo
+    for extra in ((55, 4, 7, 12, 2, 3, 128, "pos", 0.73, 0.0),
+                  (78, 5, 21, 21, 4, 2, 64, "pos", 0.64, 0.0)):
+        if extra[0] >= n:
+            out.append(extra)
     return out
 
 
