@@ -190,7 +190,9 @@ int bsga_probe_select(const bsga_shape* shape, const uint16_t* q,
  *   O[h][q] = sum_t softmax_t(Q[q].K[t] / 8) V[t],  LSE[h][q] = log sum_t e^..
  * over the patch tokens t of the blocks col_idx[row_ptr[h*B+i] ..).  Writes
  * only the patch rows of o and lse (special rows untouched).  An empty row
- * gives O = 0, LSE = -inf.  bf16 MFMA, float32 online softmax. */
+ * gives O = 0, LSE = -inf.  bf16 MFMA, float32 online softmax; P enters the
+ * P V product as bf16, or as a bf16 pair hi + lo in a row of at most 2048
+ * keys (few keys: each weight's rounding would weigh on the output). */
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q,
                      const uint16_t* k, const uint16_t* v,
                      const int32_t* row_ptr, const int32_t* col_idx,
@@ -308,6 +310,8 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     (split over key ranges, partial results combined by log-sum-exp in a
  *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and
  *     writes its row of o/lse.
+ * Patch rows of at most 2048 keys in all feed P to the P V product as a
+ * bf16 pair hi + lo, as in bsga_sparse_attn.
  * The two calls write disjoint rows and may run in either order (with
  * different workspaces if they overlap). */
 int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q,
