@@ -467,7 +467,7 @@ def main():
         "density": round(density, 4),
         "roofline": {"bound": "mfma",
                      "kernel": "attn_kernel<128, 128, kSparseTail> + tail_merge_kernel "
-                               "+ short-row pass (bsga_patch_rows_packed)",
+                               "(bsga_patch_rows_packed)",
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
                      "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic()},

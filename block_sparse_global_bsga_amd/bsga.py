@@ -60,7 +60,7 @@ _lib.bsga_csr_capacity.argtypes = [_sp, ctypes.POINTER(ctypes.c_int64)]
 _lib.bsga_redistribute.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.c_double,
                                    ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
 _lib.bsga_workspace_bytes.argtypes = [_sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
-_lib.bsga_predict_mask.argtypes = [_sp, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.bsga_predict_mask.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
                              ctypes.c_int64, _p, ctypes.c_size_t, _p]
 _lib.bsga_probe_select.argtypes = [_sp, _p, _p, ctypes.c_int32, _p, _p, _p, ctypes.c_int64, _p,
@@ -192,13 +192,16 @@ def _ws_len(ws: torch.Tensor) -> int:
 
 def predict_mask(shape: LayerShape, q: torch.Tensor, k: torch.Tensor, *,
                  probs: Optional[torch.Tensor] = None, want_means: bool = False,
-                 ws: Optional[torch.Tensor] = None):
-    """Returns probs [H][B][B] float32 (and Qbar, Kbar [H][B][64] if asked)."""
+                 want_scores: bool = False, ws: Optional[torch.Tensor] = None):
+    """Returns probs [H][B][B] float32, or a tuple (probs, then the pooled
+    scores S [H][B][B] if want_scores, then Qbar, Kbar [H][B][64] if
+    want_means)."""
     _bf16(q, "q", shape), _bf16(k, "k", shape)
     dev = q.device
     B = num_blocks(shape)
     if probs is None:
         probs = torch.empty((shape.heads, B, B), dtype=torch.float32, device=dev)
+    scores = torch.empty_like(probs) if want_scores else None
     qbar = kbar = None
     if want_means:
         qbar = torch.empty((shape.heads, B, 64), dtype=torch.float32, device=dev)
@@ -206,9 +209,13 @@ def predict_mask(shape: LayerShape, q: torch.Tensor, k: torch.Tensor, *,
     if ws is None:
         ws = workspace(shape, OP_PREDICT_MASK, dev)
     _check(_lib.bsga_predict_mask(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(probs),
-                                  _ptr(qbar), _ptr(kbar), _ws_ptr(ws), _ws_len(ws), _stream(dev)),
+                                  _ptr(scores), _ptr(qbar), _ptr(kbar), _ws_ptr(ws), _ws_len(ws),
+                                  _stream(dev)),
            "bsga_predict_mask")
-    return (probs, qbar, kbar) if want_means else probs
+    if not (want_means or want_scores):
+        return probs
+    out = (probs,) + ((scores,) if want_scores else ()) + ((qbar, kbar) if want_means else ())
+    return out
 
 
 def _rho_array(shape: LayerShape, rho_per_head: Optional[Sequence[float]]):

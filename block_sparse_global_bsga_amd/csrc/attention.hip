@@ -16,7 +16,12 @@
 //     holds the 16 scores of query l%32 for one half of each 32-key sub-tile.
 //   softmax in float32 (exp2 with log2(e)/8 folded into one FMA).
 //   O^T (dims x queries) += V^T P^T : P^T is exactly the accumulator layout
-//     converted to bf16 (the B operand), V^T comes from LDS (A operand).
+//     converted to float16 (the B operand), V^T comes from LDS (A operand),
+//     stored as float16 scaled by a power of two per head (see packing).
+//     float16 keeps 11 significant bits of every weight where bfloat16 keeps
+//     8, so the rounding of P before the product moves an output row by at
+//     most 2^-12 of the weighted |V| instead of 2^-9, and costs the same one
+//     v_cvt_pk_f16_f32 per two weights.
 // For P^T to be usable as the B operand without any data movement, the eight
 // keys a lane contributes to one PV instruction must be contiguous in V^T.
 // The accumulator rows of lane half hh are i = 8a + 4hh + c; loading K row
@@ -27,8 +32,9 @@
 // time, and every score needs one exp2, one FMA and one add, so the softmax
 // is kept to that minimum:
 //  * lazy running max: a tile is exponentiated against the running max
-//    directly (no rescaling of O) unless its exact max lies more than 64 log2
-//    units above it; that max is one v_max3 chain over the tile's scores;
+//    directly (no rescaling of O) unless its exact max lies more than 15 log2
+//    units above it (weights stay below 2^15, inside the float16 range); that
+//    max is one v_max3 chain over the tile's scores;
 //  * the rare block (first tile, partial tile, or such a jump) masks keys
 //    past a partial block, takes the exact max and rescales O and l; full
 //    tiles never execute any masking instructions;
@@ -43,14 +49,14 @@
 //
 // K and V are first packed (once per layer) into "packed order": patch
 // tokens, padding, special tokens, padding (each segment a multiple of 128),
-// K as rows [H][ntot_pad][64] and V transposed as [H][64][ntot_pad].  Tiles
+// K as rows [H][ntot_pad][64] (bf16) and V transposed as [H][64][ntot_pad]
+// (float16, V * 2^sigma_h with sigma_h chosen from the head's largest |V| so
+// that it lies in [2^14, 2^15); the epilogues multiply by 2^-sigma_h).  Tiles
 // reach LDS with buffer_load_dwordx4 ... lds (each lane's 16 bytes land at
 // base + 16 * lane: no staging registers, no LDS store instructions); the
 // bank swizzle is applied on the global side, the lane that fills LDS chunk
 // (row, physical chunk pc) fetching logical chunk pc ^ swizzle(row).  Every
 // wave fetches its share of both the K and the V^T tile.
-#include <type_traits>
-
 #include "bsga_internal.hpp"
 #include "tile_common.hpp"
 
@@ -70,14 +76,7 @@ namespace bsga {
 //                whole rows: the in-order dispatch then spreads that round
 //                over every slot, and concurrent pieces read the same key range
 //                of consecutive rows; tail_merge_kernel combines the pieces
-// kSparsePrecise: kSparseFused for the rows of at most kPreciseKeys keys
-//                only (every other workgroup returns at once), with P fed to
-//                the P V product as bf16 hi + lo; launched after the patch
-//                rows, it rewrites those rows
-enum Mode {
-  kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5,
-  kSparsePrecise = 6
-};
+enum Mode { kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5 };
 
 // most pieces per row of the last round (kSparseTail)
 constexpr int kMaxTailPieces = 16;
@@ -92,6 +91,7 @@ struct AttnArgs {
   float* lse;
   float* part_o;   // [H][ns_pad][nsplit][64]
   float* part_ml;  // [H][ns_pad][nsplit][2]
+  const int* vsig; // [H] power-of-two exponent of the packed V^T
   Dims d;
   int n_items;
   int q_tiles;
@@ -104,20 +104,14 @@ struct AttnArgs {
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
-// max is at most 64 log2 units above it: weights up to 2^64 are exact enough
-// in float32 and bf16, and sums over any sequence length stay far below
+// max is at most 15 log2 units above it: weights then stay below 2^15 (plus
+// the FMA's last-bit rounding), inside the float16 range (65504) the P V
+// product takes them in, and sums over any sequence length stay far below
 // float32 overflow.
-constexpr float kLazySlack = 64.f;
+constexpr float kLazySlack = 15.f;
 
 // Fourth word of a raw buffer resource (byte addressing, 32-bit data format)
 constexpr int kBufWord3 = 0x00020000;
-
-// Patch rows with at most this many keys in all (kept blocks and special
-// tiles) feed P to the P V product as a bf16 pair hi + lo (16 significant
-// bits) instead of one bf16: with few keys each weight carries a large share
-// of the output, and the single rounding (2^-9 relative) would show in it.
-// Such rows are short, so the extra products cost the layer next to nothing.
-constexpr int kPreciseKeys = 2048;
 
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).
@@ -170,7 +164,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       item = xcd_item(wg_x(), a.n_items);
       if (item < 0) return;
     }
-    if constexpr (MODE == kSparseFused || MODE == kSparseTail || MODE == kSparsePrecise) {
+    if constexpr (MODE == kSparseFused || MODE == kSparseTail) {
       h = item / d.B;
       qp0 = (item - h * d.B) * QT;
       const int r0 = a.row_ptr[item];
@@ -203,16 +197,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     nt_csr = __builtin_amdgcn_readfirstlane(nt_csr);
     tile0 = __builtin_amdgcn_readfirstlane(tile0);
   }
-  // (uniform per workgroup, before any LDS use or barrier)
-  if constexpr (MODE == kSparsePrecise) {
-    if (nt * KT > kPreciseKeys) return;
-  }
+  // 2^-sigma_h: undoes the power-of-two scale of the head's packed V^T
+  const float unscale = __builtin_amdgcn_ldexpf(1.f, -a.vsig[h]);
   // Position of tile n, in two steps so that the global load of a CSR entry
   // can be issued long before its value is consumed: tile_raw(n) loads the
   // entry (always from an in-bounds slot of the row), tile_kp0(n, raw) turns
   // it into the tile's first packed key.  Kept block j of the row covers tiles
   // j TPB .. j TPB + TPB - 1.
-  constexpr bool kCsr = MODE == kSparseFused || MODE == kSparseTail || MODE == kSparsePrecise;
+  constexpr bool kCsr = MODE == kSparseFused || MODE == kSparseTail;
   auto tile_raw = [&](int n) -> int {
     if constexpr (kCsr) {
       return nt_csr > 0 ? cols[min(n / TPB, nt_csr - 1)] : 0;
@@ -312,6 +304,9 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   auto lds_op = [&](uint32_t off) -> bf16x8 {
     return as_bf16x8(*(const u32x4*)((const char*)smem + off));
   };
+  auto lds_op16 = [&](uint32_t off) -> f16x8 {
+    return __builtin_bit_cast(f16x8, *(const u32x4*)((const char*)smem + off));
+  };
 
   // ---- softmax state of the wave's 32 query rows.  Lane half hh holds
   // dims [32hh, 32hh + 32) of query row qrow as the B operand, and the
@@ -361,8 +356,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
   // beside the P V products of the previous one).  CSR entries run two tiles
   // ahead: the entry of tile n+2 is loaded during iteration n and consumed
   // after that iteration's waits.
-  auto run_tiles = [&](int n0, int n1, auto precise_tag) {
-    constexpr bool kPrecise = decltype(precise_tag)::value;
+  auto run_tiles = [&](int n0, int n1) {
     {
       const int qtok = packed_token(qrow, d);
       const u32x4* src =
@@ -420,11 +414,11 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       for (int t = 0; t < (idle ? 0 : NS); ++t) {
         // the sub-tile's V^T operands are read first and may not be sunk, so
         // the LDS latency hides behind the exponentials
-        bf16x8 va[2], vb[2];
+        f16x8 va[2], vb[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          va[h2] = lds_op(kSlotBytes + vadr[t][h2]);
-          vb[h2] = lds_op(kSlotBytes + vadr[t][h2] + kVHalf);
+          va[h2] = lds_op16(kSlotBytes + vadr[t][h2]);
+          vb[h2] = lds_op16(kSlotBytes + vadr[t][h2] + kVHalf);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -435,17 +429,9 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
             e8[e] = fast_exp2(fmaf(s[t][8 * h2 + e], kScaleLog2, -m_run));
             ls += e8[e];
           }
-          const bf16x8 pb = __builtin_convertvector(e8, bf16x8);
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pb, o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pb, o1, 0, 0, 0);
-          if constexpr (kPrecise) {
-            f32x8 r8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r8[e] = e8[e] - (float)pb[e];
-            const bf16x8 pl = __builtin_convertvector(r8, bf16x8);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[h2], pl, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[h2], pl, o1, 0, 0, 0);
-          }
+          const f16x8 pb = __builtin_convertvector(e8, f16x8);
+          o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[h2], pb, o0, 0, 0, 0);
+          o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[h2], pb, o1, 0, 0, 0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -457,16 +443,20 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     }
   };
 
-  // ---- epilogues.  o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query row qrow].
-  // Unnormalised float32 partial of the wave's 32 rows, with the running max
-  // (log2 units, or raw-score units if `raw`) and the row sum.
+  // ---- epilogues.  o_u[4a + c] holds O^T[32u + 8a + 4hh + c][query row qrow]
+  // (times 2^sigma_h).  Unnormalised float32 partial of the wave's 32 rows (V's
+  // scale undone), with the running max (log2 units, or raw-score units if
+  // `raw`) and the row sum.
   auto store_partial = [&](float* po_base, float* pml, bool raw) {
     const float l_tot = xor32_sum(l_run);
     float4* po = (float4*)po_base;
+    const float u = unscale;
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
-      po[(8 * aa + 4 * hh) / 4] = make_float4(o0[4 * aa], o0[4 * aa + 1], o0[4 * aa + 2], o0[4 * aa + 3]);
-      po[(32 + 8 * aa + 4 * hh) / 4] = make_float4(o1[4 * aa], o1[4 * aa + 1], o1[4 * aa + 2], o1[4 * aa + 3]);
+      po[(8 * aa + 4 * hh) / 4] =
+          make_float4(o0[4 * aa] * u, o0[4 * aa + 1] * u, o0[4 * aa + 2] * u, o0[4 * aa + 3] * u);
+      po[(32 + 8 * aa + 4 * hh) / 4] =
+          make_float4(o1[4 * aa] * u, o1[4 * aa + 1] * u, o1[4 * aa + 2] * u, o1[4 * aa + 3] * u);
     }
     if (hh == 0) {
       pml[0] = raw ? m_run / kScaleLog2 : m_run;
@@ -478,7 +468,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     const float l_tot = xor32_sum(l_run);
     const int qtok = packed_token(qrow, d);
     if (qtok < 0) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? unscale / l_tot : 0.f;
     // natural-log LSE: (m_run + log2 l) ln 2
     const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     uint16_t* orow = a.o + ((size_t)h * d.n + qtok) * kHeadDim;
@@ -516,20 +506,17 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     if (hh == 0) *lrow = lse_out;
   };
 
-  if constexpr (MODE == kSparsePrecise) {
-    run_tiles(0, nt, std::true_type{});
-    store_rows();
-  } else if constexpr (MODE == kSparseTail) {
+  if constexpr (MODE == kSparseTail) {
     if (piece < 0) {
-      run_tiles(0, nt, std::false_type{});
+      run_tiles(0, nt);
       store_rows();
     } else {
-      run_tiles(nt * piece / a.tail_pieces, nt * (piece + 1) / a.tail_pieces, std::false_type{});
+      run_tiles(nt * piece / a.tail_pieces, nt * (piece + 1) / a.tail_pieces);
       const size_t row = piece_slot * QT + 32 * w + l32;
       store_partial(a.part_o + row * kHeadDim, a.part_ml + row * 2, false);
     }
   } else {
-    run_tiles(0, nt, std::false_type{});
+    run_tiles(0, nt);
     if constexpr (MODE == kSpecialSplit) {
       const int sq = qrow - d.np_pad;
       const size_t slot = ((size_t)h * d.ns_pad + sq) * a.nsplit + split;
@@ -644,29 +631,99 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
 
 // ---------------------------------------------------------------------------
 // Packing: K rows and transposed V in packed order, 64 keys per workgroup.
+//
+// V^T is stored as float16 so that the P V product can take P as float16
+// (11 significant bits).  Every bf16 value times a power of two is exact in
+// float16 inside its normal range, so the head's V is scaled by 2^sigma_h
+// with its largest |V| in [2^14, 2^15) (below the float16 maximum 65504);
+// values more than 2^28 below that maximum land among the float16 subnormals
+// with an absolute error under 2^-39 of the maximum.  sigma_h is clamped to
+// [-100, 100] (and 0 for a head without finite nonzero values).
+//
+// vmax_kernel: per (head, chunk of tokens) the largest |V| as bf16 bits
+// (the sign cleared, non-negative bf16 values order like their bit
+// patterns); pack_kernel reduces the head's chunks, derives sigma_h, and
+// writes it once per head.
+constexpr int kVmaxChunks = 64;
+
+static int vmax_chunks(const Dims& d) { return min(kVmaxChunks, (d.n + 1023) / 1024); }
+
+__global__ __launch_bounds__(256) void vmax_kernel(const uint4* __restrict__ v,
+                                                   uint32_t* __restrict__ chunk_max, Dims d,
+                                                   int nchunk) {
+  const int c = wg_x(), h = wg_y(), T = lid_x();
+  const int per = (d.n + nchunk - 1) / nchunk;
+  const int t0 = c * per, t1 = min(d.n, t0 + per);
+  const uint4* src = v + (size_t)h * d.n * 8;
+  uint32_t m = 0;
+  for (int i = t0 * 8 + T; i < t1 * 8; i += 256) {
+    const uint4 x = src[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7fffu, (w[e] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[4];
+  if ((T & 63) == 0) red[T >> 6] = m;
+  __syncthreads();
+  if (T == 0) chunk_max[h * kVmaxChunks + c] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// sigma_h from the largest |V| (bf16 bits of the absolute value)
+__device__ inline int v_sigma(uint32_t mb) {
+  if (mb == 0 || mb >= 0x7f80u) return 0;  // all zero, or inf / NaN present
+  const int e = (int)(mb >> 7) - 127;      // |V| max in [2^e, 2^(e+1)) (e = -127: subnormal)
+  return min(100, max(-100, 14 - e));
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
                                                    const uint4* __restrict__ v,
                                                    uint4* __restrict__ kp,
-                                                   uint4* __restrict__ vt, Dims d) {
+                                                   uint4* __restrict__ vt,
+                                                   const uint32_t* __restrict__ chunk_max,
+                                                   int* __restrict__ vsig, Dims d, int nchunk) {
   __shared__ uint16_t sv[64][66];
+  __shared__ int sig_s;
   const int kp0 = wg_x() * 64, h = wg_y(), T = lid_x();
+  if (T < 64) {
+    uint32_t m = T < nchunk ? chunk_max[h * kVmaxChunks + T] : 0u;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (T == 0) {
+      sig_s = v_sigma(m);
+      if (wg_x() == 0) vsig[h] = sig_s;
+    }
+  }
   const size_t src_head = (size_t)h * d.n * 8;
+  uint4 vv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = T + 256 * i;
     const int row = c >> 3, ch = c & 7;
     const int tok = packed_token(kp0 + row, d);
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    uint4 kv = make_uint4(0, 0, 0, 0);
+    vv[i] = make_uint4(0, 0, 0, 0);
     if (tok >= 0) {
       kv = k[src_head + (size_t)tok * 8 + ch];
-      vv = v[src_head + (size_t)tok * 8 + ch];
+      vv[i] = v[src_head + (size_t)tok * 8 + ch];
     }
     kp[((size_t)h * d.ntot_pad + kp0 + row) * 8 + ch] = kv;
-    const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+  }
+  __syncthreads();
+  const int sig = sig_s;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int row = c >> 3, ch = c & 7;
+    const uint32_t wv[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sv[row][ch * 8 + 2 * e] = (uint16_t)(wv[e] & 0xffff);
-      sv[row][ch * 8 + 2 * e + 1] = (uint16_t)(wv[e] >> 16);
+      // bf16 -> float32 (exact) -> times 2^sigma (exact) -> float16 (exact in range)
+      const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(wv[e] << 16), sig);
+      const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(wv[e] & 0xffff0000u), sig);
+      sv[row][ch * 8 + 2 * e] = __builtin_bit_cast(uint16_t, (_Float16)lo);
+      sv[row][ch * 8 + 2 * e + 1] = __builtin_bit_cast(uint16_t, (_Float16)hi);
     }
   }
   __syncthreads();
@@ -682,14 +739,34 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
   }
 }
 
-size_t pack_bytes(const Dims& d) {
+// Packed buffer: K rows, V^T, then the per-head exponent table (H ints) and
+// the per-(head, chunk) maxima of vmax_kernel (H x 64 uint32), each region
+// 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static size_t pack_kv_bytes(const Dims& d) {
   return 2 * (size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t);
+}
+static int* packed_vsig(const Dims& d, const uint16_t* kp) {
+  return (int*)((char*)kp + pack_kv_bytes(d));
+}
+static uint32_t* packed_chunk_max(const Dims& d, const uint16_t* kp) {
+  return (uint32_t*)((char*)kp + pack_kv_bytes(d) + align256((size_t)d.H * sizeof(int)));
+}
+
+size_t pack_bytes(const Dims& d) {
+  return pack_kv_bytes(d) + align256((size_t)d.H * sizeof(int)) +
+         align256((size_t)d.H * kVmaxChunks * sizeof(uint32_t));
 }
 
 hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint16_t* kp,
                        uint16_t* vt, hipStream_t st) {
-  pack_kernel<<<dim3(d.ntot_pad / 64, d.H), 256, 0, st>>>((const uint4*)k, (const uint4*)v,
-                                                          (uint4*)kp, (uint4*)vt, d);
+  const int nchunk = vmax_chunks(d);
+  uint32_t* cm = packed_chunk_max(d, kp);
+  vmax_kernel<<<dim3(nchunk, d.H), 256, 0, st>>>((const uint4*)v, cm, d, nchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  pack_kernel<<<dim3(d.ntot_pad / 64, d.H), 256, 0, st>>>(
+      (const uint4*)k, (const uint4*)v, (uint4*)kp, (uint4*)vt, cm, packed_vsig(d, kp), d, nchunk);
   return hipGetLastError();
 }
 
@@ -704,13 +781,6 @@ template <int MODE>
 static hipError_t run_attn_b(const Dims& d, const AttnArgs& a, hipStream_t st) {
   return d.b == 64 ? run_attn<64, 64, MODE>(a, st) : run_attn<128, 128, MODE>(a, st);
 }
-// the short rows again with P as bf16 hi + lo, at two waves per SIMD (room
-// for the extra operands without spilling)
-static hipError_t run_precise(const Dims& d, const AttnArgs& a, hipStream_t st) {
-  return d.b == 64 ? run_attn<64, 64, kSparsePrecise, 2>(a, st)
-                   : run_attn<128, 128, kSparsePrecise, 2>(a, st);
-}
-
 
 static AttnArgs base_args(const Dims& d, const uint16_t* q, const uint16_t* kp,
                           const uint16_t* vt, uint16_t* o, float* lse) {
@@ -720,6 +790,7 @@ static AttnArgs base_args(const Dims& d, const uint16_t* q, const uint16_t* kp,
   a.vt = vt;
   a.o = o;
   a.lse = lse;
+  a.vsig = packed_vsig(d, kp);
   a.d = d;
   return a;
 }
@@ -732,8 +803,7 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q, const uint16_t* 
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
   a.patch_only = 1;
-  const hipError_t e = run_attn_b<kSparseFused>(d, a, st);
-  return e != hipSuccess ? e : run_precise(d, a, st);
+  return run_attn_b<kSparseFused>(d, a, st);
 }
 
 // kSparseTail plan: slots per XCD (three 128 x 128 workgroups per compute
@@ -827,12 +897,10 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
       if (e != hipSuccess) return e;
       tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
           a.part_o, a.part_ml, o, lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem);
-      e = hipGetLastError();
-      return e != hipSuccess ? e : run_precise(d, a, st);
+      return hipGetLastError();
     }
   }
-  const hipError_t e = run_attn_b<kSparseFused>(d, a, st);
-  return e != hipSuccess ? e : run_precise(d, a, st);
+  return run_attn_b<kSparseFused>(d, a, st);
 }
 
 struct SplitPlan {

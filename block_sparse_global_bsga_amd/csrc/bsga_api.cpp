@@ -204,11 +204,14 @@ int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes) {
 }
 
 int bsga_predict_mask(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, float* probs,
-                      float* qbar, float* kbar, void* ws, size_t ws_bytes, void* stream) {
+                      float* scores, float* qbar, float* kbar, void* ws, size_t ws_bytes,
+                      void* stream) {
   BSGA_TRY(check_shape(shape));
   const Dims d = make_dims(*shape);
   BSGA_TRY(check_qk(q, k));
   BSGA_TRY(check_ptr(probs, 4));
+  if (scores) BSGA_TRY(check_ptr(scores, 4));
+  if (scores == probs) return BSGA_ERR_INVALID_ARG;
   if (qbar) BSGA_TRY(check_ptr(qbar, 4));
   if (kbar) BSGA_TRY(check_ptr(kbar, 4));
   BSGA_TRY(check_ws(d, BSGA_OP_PREDICT_MASK, ws, ws_bytes));
@@ -217,7 +220,7 @@ int bsga_predict_mask(const bsga_shape* shape, const uint16_t* q, const uint16_t
   float* kb = kbar ? kbar : (float*)((char*)ws + half);
   hipStream_t st = (hipStream_t)stream;
   BSGA_TRY(hip_status(launch_pool(d, q, k, qb, kb, st)));
-  BSGA_TRY(hip_status(launch_scores(d, qb, kb, probs, st)));
+  BSGA_TRY(hip_status(launch_scores(d, qb, kb, probs, scores, st)));
   return hip_status(launch_softmax(d, probs, st));
 }
 
@@ -452,7 +455,7 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, co
   float* qb = (float*)scratch;
   float* kb = (float*)(scratch + half);
   BSGA_TRY(hip_status(launch_pool(d, q, k, qb, kb, st)));
-  BSGA_TRY(hip_status(launch_scores(d, qb, kb, probs, st)));
+  BSGA_TRY(hip_status(launch_scores(d, qb, kb, probs, nullptr, st)));
   BSGA_TRY(hip_status(launch_softmax(d, probs, st)));
   BSGA_TRY(hip_status(launch_select(d, probs, sp, row_ptr, col_idx, scratch, st)));
   BSGA_TRY(hip_status(launch_pack(d, k, v, kp, vt, st)));

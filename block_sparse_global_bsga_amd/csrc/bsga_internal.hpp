@@ -10,6 +10,7 @@
 namespace bsga {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -110,7 +111,7 @@ __device__ inline float bf16_to_f32(uint16_t b) {
 hipError_t launch_pool(const Dims& d, const uint16_t* q, const uint16_t* k,
                        float* qbar, float* kbar, hipStream_t st);
 hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar,
-                         float* probs, hipStream_t st);
+                         float* probs, float* scores, hipStream_t st);
 hipError_t launch_softmax(const Dims& d, float* probs, hipStream_t st);
 
 struct SelectParams {

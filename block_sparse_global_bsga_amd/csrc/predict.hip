@@ -114,9 +114,12 @@ __device__ inline void split3(const float* x, bf16x8& a, bf16x8& b, bf16x8& c) {
   c = __builtin_convertvector(r2, bf16x8);
 }
 
+// s receives S (the softmax then runs on it in place); s2, when not null, a
+// copy of S for the caller.
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
-                                                     float* __restrict__ s, Dims d) {
+                                                     float* __restrict__ s, float* __restrict__ s2,
+                                                     Dims d) {
   const int h = blockIdx.z;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -150,15 +153,19 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (i < d.B) s[((size_t)h * d.B + i) * d.B + j] = acc[r] * 0.125f;
+      if (i < d.B) {
+        const size_t at = ((size_t)h * d.B + i) * d.B + j;
+        s[at] = acc[r] * 0.125f;
+        if (s2) s2[at] = acc[r] * 0.125f;
+      }
     }
   }
 }
 
 hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar,
-                         float* probs, hipStream_t st) {
+                         float* probs, float* scores, hipStream_t st) {
   const int t = (d.B + 63) / 64;
-  scores_kernel<<<dim3(t, t, d.H), 256, 0, st>>>(qbar, kbar, probs, d);
+  scores_kernel<<<dim3(t, t, d.H), 256, 0, st>>>(qbar, kbar, probs, scores, d);
   return hipGetLastError();
 }
 

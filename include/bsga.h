@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BSGA_VERSION 1
+#define BSGA_VERSION 2
 #define BSGA_MAX_HEADS 256     /* per-head budget table size */
 #define BSGA_MAX_BLOCKS 4096   /* largest B accepted by bsga_select */
 
@@ -132,15 +132,17 @@ int bsga_workspace_bytes(const bsga_shape* shape, int op, size_t* bytes);
  *   Qbar[h][i] = mean of the patch rows of block i of Q (likewise Kbar),
  *   S = Qbar Kbar^T / sqrt(64), probs[h][i][:] = softmax of S[h][i][:].
  * q, k: [H][N][64] bf16.  probs: [H][B][B] float32 (output).
+ * scores: optional [H][B][B] float32 output of S itself (NULL to skip).
  * qbar, kbar: optional [H][B][64] float32 outputs (NULL to skip).
  * Pooling accumulates in float32; the pooled-score product runs on bf16
  * MFMA on a three-way bf16 split of the float32 means (x = x1 + x2 + x3, six
- * cross products; error near that of a float32 product); the softmax is
- * float32. */
+ * cross products of exact float32 terms accumulated in float32: error near
+ * that of a float32 dot product); the softmax is float32.  The optional
+ * outputs must be 4-byte aligned and must not overlap probs. */
 int bsga_predict_mask(const bsga_shape* shape, const uint16_t* q,
-                      const uint16_t* k, float* probs, float* qbar,
-                      float* kbar, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      const uint16_t* k, float* probs, float* scores,
+                      float* qbar, float* kbar, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Two-threshold block selection ([BSGA] key design 2; [HeSS] per-head
  * budget).  For every row (h, i) of probs: rank the B key blocks by
@@ -190,9 +192,11 @@ int bsga_probe_select(const bsga_shape* shape, const uint16_t* q,
  *   O[h][q] = sum_t softmax_t(Q[q].K[t] / 8) V[t],  LSE[h][q] = log sum_t e^..
  * over the patch tokens t of the blocks col_idx[row_ptr[h*B+i] ..).  Writes
  * only the patch rows of o and lse (special rows untouched).  An empty row
- * gives O = 0, LSE = -inf.  bf16 MFMA, float32 online softmax; P enters the
- * P V product as bf16, or as a bf16 pair hi + lo in a row of at most 2048
- * keys (few keys: each weight's rounding would weigh on the output). */
+ * gives O = 0, LSE = -inf.  MFMA products with float32 accumulation and a
+ * float32 online softmax: Q K^T in bf16; P enters the P V product as
+ * float16 (11 significant bits; weights never exceed 2^15), V as float16
+ * scaled per head by a power of two (exact for bf16 values; see
+ * bsga_pack_kv). */
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q,
                      const uint16_t* k, const uint16_t* v,
                      const int32_t* row_ptr, const int32_t* col_idx,
@@ -263,10 +267,18 @@ int bsga_attn_backward(const bsga_shape* shape, const uint16_t* q,
  * next multiple of 128, then the N_s special tokens, zero rows up to the next
  * multiple of 128 (Ntot_pad keys in all) — and stored as
  *   K rows   [H][Ntot_pad][64] bf16, followed by
- *   V^T      [H][64][Ntot_pad] bf16 (V transposed: keys contiguous).
- * Packing once per layer lets the sparse, special and dense calls share it.
- * kv_packed must be a 256-byte aligned device buffer of at least
- * bsga_packed_kv_bytes bytes. */
+ *   V^T      [H][64][Ntot_pad] float16 (V transposed: keys contiguous),
+ *            holding V[h] * 2^sigma_h, where sigma_h puts the head's largest
+ *            |V| in [2^14, 2^15) (clamped to [-100, 100]; 0 when the head has
+ *            no finite nonzero value), followed by
+ *   sigma    [H] int32 (256-byte aligned), and a per-head scratch table the
+ *            packing uses to find each head's largest |V|.
+ * A bf16 value times a power of two is exact in float16 inside its normal
+ * range, so the scaled copy loses nothing but values more than 2^28 below the
+ * head's largest |V| (absolute error below 2^-39 of it).  Packing (two
+ * kernels: the per-head maximum, then the copy) once per layer lets the
+ * sparse, special and dense calls share it.  kv_packed must be a 256-byte
+ * aligned device buffer of at least bsga_packed_kv_bytes bytes. */
 int bsga_packed_kv_bytes(const bsga_shape* shape, size_t* bytes);
 int bsga_pack_kv(const bsga_shape* shape, const uint16_t* k, const uint16_t* v,
                  void* kv_packed, size_t kv_bytes, void* stream);
@@ -310,8 +322,7 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     (split over key ranges, partial results combined by log-sum-exp in a
  *     workspace of bsga_workspace_bytes(BSGA_OP_SPECIAL_DENSE_PACKED)) and
  *     writes its row of o/lse.
- * Patch rows of at most 2048 keys in all feed P to the P V product as a
- * bf16 pair hi + lo, as in bsga_sparse_attn.
+ * Precision as in bsga_sparse_attn (P enters the P V product as float16).
  * The two calls write disjoint rows and may run in either order (with
  * different workspaces if they overlap). */
 int bsga_patch_rows_packed(const bsga_shape* shape, const uint16_t* q,

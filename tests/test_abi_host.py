@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bsga.version() == 1
+    assert bsga.version() == 2
     for s in range(6):
         assert bsga.status_string(s)
     assert bsga.status_string(99) == "unknown status"
@@ -213,13 +213,16 @@ def test_validation_before_launch():
     ws = bsga.workspace_bytes(shape, bsga.OP_LAYER)
     cap = bsga.csr_capacity(shape)
     # null and misaligned tensors
-    assert lib.bsga_predict_mask(sh, None, FAKE, FAKE, None, None, FAKE, ws, None) == bsga.ERR_INVALID_ARG
-    assert lib.bsga_predict_mask(sh, FAKE + 2, FAKE, FAKE, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
-    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE + 1, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_predict_mask(sh, None, FAKE, FAKE, None, None, None, FAKE, ws, None) == bsga.ERR_INVALID_ARG
+    assert lib.bsga_predict_mask(sh, FAKE + 2, FAKE, FAKE, None, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE + 1, None, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    # the optional score output: aligned, and not the probabilities' own buffer
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, FAKE + 2, None, None, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == bsga.ERR_INVALID_ARG
     # workspace: missing, short, misaligned
-    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, None, ws, None) == bsga.ERR_WORKSPACE
-    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, FAKE, 16, None) == bsga.ERR_WORKSPACE
-    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, FAKE + 16, ws, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, None, None, ws, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, None, FAKE, 16, None) == bsga.ERR_WORKSPACE
+    assert lib.bsga_predict_mask(sh, FAKE, FAKE, FAKE, None, None, None, FAKE + 16, ws, None) == bsga.ERR_WORKSPACE
     # select: rho / tau / capacity
     for rho, tau in ((-0.5, 0.9), (1.01, 0.9), (float("nan"), 0.9), (0.5, float("nan"))):
         assert lib.bsga_select(sh, FAKE, None, rho, tau, FAKE, FAKE, cap, FAKE, ws, None) \

@@ -88,7 +88,7 @@ def test_pooled_specials_layer(lib, index):
     o, lse = from_dev_bf16(bufs.o), bufs.lse.cpu().numpy()
     rng = np.random.default_rng(9)
     acc = cnt = 0.0
-    worst_o = worst_l = 0.0
+    worst_o = worst_l = worst_raw = 0.0
     for h in range(cfg.heads):
         qh, kh, vh = head_f64(x, h)
         blocks = sorted({0, B - 1} | set(rng.choice(B, size=min(B, 4), replace=False).tolist()))
@@ -98,8 +98,9 @@ def test_pooled_specials_layer(lib, index):
         d = np.stack([r[0] for r in dense.values()])
         acc += float(np.sum(d ** 2))
         cnt += d.size
-        eo, el, _, _, _ = compare_rows(out, o[h], lse[h])
-        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        eo, el, _, _, raw = compare_rows(out, o[h], lse[h])
+        worst_o, worst_l, worst_raw = max(worst_o, eo), max(worst_l, el), max(worst_raw, raw)
     rms = (acc / cnt) ** 0.5
-    say(f"   err {worst_o / rms:.3e} rms(O_dense), dLSE {worst_l:.2e}")
+    say(f"   err beyond bf16 rounding {worst_o / rms:.3e} rms(O_dense) (plain "
+        f"{worst_raw / rms:.3e}), dLSE {worst_l:.2e}")
     assert worst_o <= 2e-2 * rms and worst_l <= 2e-3

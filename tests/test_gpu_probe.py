@@ -106,7 +106,7 @@ def test_probe_attention(lib, name):
     o_h, lse_h = from_dev_bf16(o), lse.cpu().numpy()
     B = lib.num_blocks(shape)
     rng = np.random.default_rng(31)
-    worst_o = worst_l = 0.0
+    worst_o = worst_l = worst_raw = 0.0
     acc = cnt = 0.0
     for h in range(cfg.heads):
         blocks = sorted({0, B - 1} | set(rng.choice(B, size=min(B, 3), replace=False).tolist()))
@@ -116,8 +116,9 @@ def test_probe_attention(lib, name):
         d = np.stack([r[0] for r in dense.values()])
         acc += float(np.sum(d ** 2))
         cnt += d.size
-        eo, el, _, _, _ = compare_rows(out, o_h[h], lse_h[h])
-        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        eo, el, _, _, raw = compare_rows(out, o_h[h], lse_h[h])
+        worst_o, worst_l, worst_raw = max(worst_o, eo), max(worst_l, el), max(worst_raw, raw)
     rms = (acc / cnt) ** 0.5
-    say(f"[probe-attn] {name} topk={topk}: err {worst_o / rms:.3e} rms(O_dense), dLSE {worst_l:.2e}")
+    say(f"[probe-attn] {name} topk={topk}: err beyond bf16 rounding {worst_o / rms:.3e} "
+        f"rms(O_dense) (plain {worst_raw / rms:.3e}), dLSE {worst_l:.2e}")
     assert worst_o <= 2e-2 * rms and worst_l <= 2e-3
