@@ -31,6 +31,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = r
  OP_PATCH_ROWS_PACKED) = range(11)
 MAX_HEADS = 256
 MAX_BLOCKS = 4096
+SELECT_STATIC_MAX_ROWS = 65536
 
 EXPORTS = [
     "bsga_version", "bsga_status_string", "bsga_num_blocks", "bsga_keep_count",
@@ -39,7 +40,7 @@ EXPORTS = [
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
     "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select", "bsga_nmse",
-    "bsga_attn_backward",
+    "bsga_attn_backward", "bsga_select_static",
 ]
 
 
@@ -63,6 +64,8 @@ _lib.bsga_workspace_bytes.argtypes = [_sp, ctypes.c_int, ctypes.POINTER(ctypes.c
 _lib.bsga_predict_mask.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.bsga_select.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
                              ctypes.c_int64, _p, ctypes.c_size_t, _p]
+_lib.bsga_select_static.argtypes = [_sp, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
+                                    ctypes.c_int64, _p]
 _lib.bsga_probe_select.argtypes = [_sp, _p, _p, ctypes.c_int32, _p, _p, _p, ctypes.c_int64, _p,
                                    ctypes.c_size_t, _p]
 _lib.bsga_nmse.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -247,6 +250,28 @@ def select(shape: LayerShape, probs: torch.Tensor, rho: float, tau: float,
     _check(_lib.bsga_select(ctypes.byref(shape.c()), _ptr(probs), rp, float(rho), float(tau),
                             _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ws_ptr(ws),
                             _ws_len(ws), _stream(dev)), "bsga_select")
+    del keep
+    return row_ptr, col_idx
+
+
+def select_static(shape: LayerShape, probs: torch.Tensor, rho: float, tau: float,
+                  rho_per_head: Optional[Sequence[float]] = None, *,
+                  row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None):
+    """bsga_select_static: the selection without a workspace (the library's own
+    per-GPU scratch).  Returns (row_ptr, col_idx) like select()."""
+    dev = probs.device
+    B = num_blocks(shape)
+    if probs.dtype != torch.float32 or tuple(probs.shape) != (shape.heads, B, B) \
+            or not probs.is_contiguous():
+        raise ValueError("probs must be contiguous float32 [H][B][B]")
+    if row_ptr is None:
+        row_ptr = torch.empty(shape.heads * B + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(csr_capacity(shape), dtype=torch.int32, device=dev)
+    keep, rp = _rho_array(shape, rho_per_head)
+    _check(_lib.bsga_select_static(ctypes.byref(shape.c()), _ptr(probs), rp, float(rho),
+                                   float(tau), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                   _stream(dev)), "bsga_select_static")
     del keep
     return row_ptr, col_idx
 

@@ -238,6 +238,24 @@ int bsga_select(const bsga_shape* shape, const float* probs, const double* rho_p
   return hip_status(launch_select(d, probs, sp, row_ptr, col_idx, ws, (hipStream_t)stream));
 }
 
+int bsga_select_static(const bsga_shape* shape, const float* probs, const double* rho_per_head,
+                       double rho, double tau, int32_t* row_ptr, int32_t* col_idx,
+                       int64_t col_capacity, void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_select_shape(d));
+  if ((int64_t)d.H * d.B > BSGA_SELECT_STATIC_MAX_ROWS) return BSGA_ERR_UNSUPPORTED;
+  BSGA_TRY(check_ptr(probs, 4));
+  BSGA_TRY(check_csr(d, row_ptr, col_idx, col_capacity));
+  SelectParams sp;
+  BSGA_TRY(fill_select_params(d, rho_per_head, rho, tau, &sp));
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  BSGA_TRY(hip_status(select_static_scratch(&scratch, &scratch_bytes)));
+  if (ws_select(d) > scratch_bytes) return BSGA_ERR_UNSUPPORTED;
+  return hip_status(launch_select(d, probs, sp, row_ptr, col_idx, scratch, (hipStream_t)stream));
+}
+
 int bsga_probe_select(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, int32_t topk,
                       float* scores, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                       void* ws, size_t ws_bytes, void* stream) {

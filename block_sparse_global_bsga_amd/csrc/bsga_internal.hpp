@@ -123,6 +123,10 @@ hipError_t launch_select(const Dims& d, const float* probs,
                          const SelectParams& sp, int32_t* row_ptr,
                          int32_t* col_idx, void* ws, hipStream_t st);
 
+// device address and size of the selection scratch array of the current
+// device (bsga_select_static)
+hipError_t select_static_scratch(void** out, size_t* bytes);
+
 size_t probe_workspace(const Dims& d);
 hipError_t launch_probe_select(const Dims& d, const uint16_t* q, const uint16_t* k, int topk,
                                float* scores, int32_t* row_ptr, int32_t* col_idx, void* ws,

@@ -19,6 +19,8 @@
 // parallel scan here and a sequential sum reach identical decisions unless
 // the crossing value itself is below 2^-29 (tau within ~B*2^-29 of the row's
 // total).
+#include <mutex>
+
 #include "bsga_internal.hpp"
 
 namespace bsga {
@@ -309,6 +311,49 @@ hipError_t launch_select(const Dims& d, const float* probs, const SelectParams& 
 hipError_t launch_scan_counts(const int32_t* counts, int rows, int32_t* row_ptr, hipStream_t st) {
   scan_counts_kernel<<<1, 1024, 0, st>>>(counts, rows, row_ptr);
   return hipGetLastError();
+}
+
+}  // namespace bsga
+
+namespace bsga {
+
+// ---------------------------------------------------------------------------
+// Selection without a caller workspace (bsga_select_static).  The per-row
+// counts and thresholds live in `scratch`, a file-scope device array: one
+// copy per GPU, held until the process ends, shared by every such call on
+// that GPU (calls that overlap on one GPU race on it).  Each row kernel
+// writes its row's count and threshold before the scan and the compaction
+// read them, so nothing in it has to start at zero and leftovers of an
+// earlier call are never read.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+static_assert((((size_t)BSGA_SELECT_STATIC_MAX_ROWS * sizeof(int32_t) + 255) & ~(size_t)255) +
+                      (size_t)BSGA_SELECT_STATIC_MAX_ROWS * sizeof(uint64_t) <=
+                  kStaticScratchBytes,
+              "scratch holds the largest accepted selection");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t select_static_scratch(void** out, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
 }
 
 }  // namespace bsga

@@ -162,6 +162,24 @@ int bsga_select(const bsga_shape* shape, const float* probs,
                 int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* bsga_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, semantics and results
+ * as bsga_select (bit-identical CSR).  Its scratch (per-row counts and
+ * thresholds) is a 1 MiB array the library holds in device memory, one copy
+ * per GPU, kept until the process ends; the call allocates nothing.  Every
+ * such call on one GPU shares that array, so calls that may overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller; a call leaves the array's contents behind, and the next call
+ * never reads them.  Limit: H * B <= BSGA_SELECT_STATIC_MAX_ROWS rows
+ * (BSGA_ERR_UNSUPPORTED beyond it, checked before anything is launched);
+ * BSGA_ERR_HIP if the array's device address cannot be found. */
+#define BSGA_SELECT_STATIC_MAX_ROWS 65536
+int bsga_select_static(const bsga_shape* shape, const float* probs,
+                       const double* rho_per_head, double rho, double tau,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                       void* stream);
+
 /* Query-probe Top-K block selection ("SAF3R: Dynamic Sparse Attention for
  * Feed-Forward 3D Reconstruction Transformers", cited as [SAF3R], section 4:
  * the query-probe Top-K kernel for heads whose queries share a few dominant

@@ -239,6 +239,18 @@ def test_validation_before_launch():
     assert lib.bsga_special_dense(sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == bsga.ERR_WORKSPACE
     assert lib.bsga_layer(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE, FAKE,
                           FAKE, ws - 1, None) == bsga.ERR_WORKSPACE
+    # the selection without a workspace: its row limit, then the usual checks
+    # (all before any HIP call)
+    over = S(1, 128 * 1025, 0, 64, 128)  # 64 heads x 1025 blocks > 65,536 rows
+    assert bsga.num_blocks(over) * 64 > bsga.SELECT_STATIC_MAX_ROWS
+    assert lib.bsga_select_static(ctypes.byref(over.c()), FAKE, None, 0.5, 0.9, FAKE, FAKE,
+                                  1 << 40, None) == bsga.ERR_UNSUPPORTED
+    assert lib.bsga_select_static(sh, FAKE, None, 1.5, 0.9, FAKE, FAKE, cap, None) \
+        == bsga.ERR_INVALID_ARG
+    assert lib.bsga_select_static(sh, FAKE + 2, None, 0.5, 0.9, FAKE, FAKE, cap, None) \
+        == bsga.ERR_MISALIGNED
+    assert lib.bsga_select_static(sh, FAKE, None, 0.5, 0.9, FAKE, FAKE, cap - 1, None) \
+        == bsga.ERR_INVALID_ARG
     # selection beyond the sort's capacity
     big = S(1, 64 * 5000, 0, 1, 64)
     assert lib.bsga_select(ctypes.byref(big.c()), FAKE, None, 0.5, 0.9, FAKE, FAKE, 1 << 40, FAKE,
