@@ -117,11 +117,14 @@ def computed_entries(row_ptr, col_idx, n_patch, block, heads, n_special):
     return pp, sp
 
 
-def cpu_baseline(x, seconds):
+def cpu_baseline(x, seconds, layer_entries):
     """The oracle as it stands, on a bounded sample of the same layer: the
     mask of head 0 (pooling, scores, softmax, selection over all its rows)
     plus the attention of as many query blocks of head 0 as fit in about
-    `seconds` (patch queries over kept blocks and special keys)."""
+    `seconds` (patch queries over kept blocks and special keys).  Also an
+    extrapolated time for the whole layer: the head's mask time times the
+    heads, plus the sample's time per computed entry times the layer's
+    computed entries (`layer_entries`, every head, special rows included)."""
     from threadpoolctl import threadpool_info
     from block_sparse_global_bsga_amd import synth
     from oracle import bsga_oracle as O
@@ -131,26 +134,36 @@ def cpu_baseline(x, seconds):
     t0 = time.perf_counter()
     _, _, _, p = O.predict_head(q[patch], k[patch], cfg.block)
     B = p.shape[0]
-    kk = O.keep_count(B, cfg.rho)
+    rho0 = float(x.rho_per_head[0]) if x.rho_per_head is not None else cfg.rho
+    kk = O.keep_count(B, rho0)
     kept = [O.select_row(p[i].astype(np.float32), kk, cfg.tau)[0] for i in range(B)]
+    t_mask = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     order = rng.permutation(B)
     size = np.array([O.block_members(cfg.n_patch, cfg.block, j).shape[0] for j in range(B)])
     entries, done = 0, 0
+    t1 = time.perf_counter()
     while done < B and (done < 4 or time.perf_counter() - t0 < seconds):
         i = int(order[done])
         O.layer_head(q, k, v, cfg.frames, cfg.patches_per_frame, cfg.special_per_frame,
                      cfg.block, kept, query_blocks=[i], special_queries=False)
         entries += int(size[i]) * (int(size[kept[i]].sum()) + cfg.n_special)
         done += 1
-    dt = time.perf_counter() - t0
+    t_attn = time.perf_counter() - t1
+    dt = t_mask + t_attn
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    layer_ms = (cfg.heads * t_mask + t_attn / entries * layer_entries) * 1e3
     return {"value": 4 * HEAD_DIM * entries / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"numpy float64 oracle, head 0 of the same layer: full mask prediction "
-                      f"and selection ({B} rows) plus attention of {done} of {B} query blocks "
-                      f"(patch queries over kept blocks + special keys), {dt:.1f} s; effective "
-                      f"FLOP/s on the attention entries computed"}
+                      f"and selection ({B} rows, {t_mask:.2f} s) plus attention of {done} of {B} "
+                      f"query blocks (patch queries over kept blocks + special keys, "
+                      f"{t_attn:.1f} s); effective FLOP/s on the attention entries computed",
+            "ms_per_layer_extrapolated": round(layer_ms, 1),
+            "extrapolation": f"extrapolated, not measured: {cfg.heads} heads x the head-0 mask "
+                             f"time + the sample's time per computed entry x the layer's "
+                             f"{layer_entries} computed entries (all heads, special rows "
+                             f"included)"}
 
 
 def main():
@@ -443,7 +456,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("# timing the oracle on a CPU sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(x, args.cpu_seconds)
+        cpu = cpu_baseline(x, args.cpu_seconds, pp + sp)
 
     out = {
         "metric": "ms/global-attn layer + effective TFLOP/s (frac bf16 peak), 32 frames rho=0.75",

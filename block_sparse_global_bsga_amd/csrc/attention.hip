@@ -101,6 +101,14 @@ struct AttnArgs {
   int tail_m;        // kSparseTail: workgroup slots per XCD (one round)
   int tail_pieces;   // kSparseTail: pieces per row of the last round
   int patch_only;    // kSparseFused: skip the special tiles
+  // b = 64 run as aligned pairs (attn_kernel's PAIR, kSparseFused /
+  // kSparseTail at QT = KT = 128): query tile I holds query blocks 2I, 2I + 1, key tile J key blocks
+  // 2J, 2J + 1; pair_cols[(h Bp + I) Bp + n] = J | act << 28 lists, in
+  // ascending J, the key tiles that hold a block kept by either query block,
+  // act bit 2 hq + kh set iff query block 2I + hq keeps key block 2J + kh;
+  // pair_len[h Bp + I] entries; Bp = ceil(B / 2)
+  const int32_t* pair_cols;
+  const int32_t* pair_len;
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
@@ -115,7 +123,8 @@ constexpr int kBufWord3 = 0x00020000;
 
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).
-template <int QT, int KT, int MODE, int WPE>
+// PAIR: b = 64 blocks run as aligned pairs (AttnArgs::pair) on QT = KT = 128
+template <int QT, int KT, int MODE, int WPE, bool PAIR = false>
 __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_kernel(
     AttnArgs a) {
   constexpr int NW = QT / 32;       // waves
@@ -165,11 +174,19 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       if (item < 0) return;
     }
     if constexpr (MODE == kSparseFused || MODE == kSparseTail) {
-      h = item / d.B;
-      qp0 = (item - h * d.B) * QT;
-      const int r0 = a.row_ptr[item];
-      cols = a.col_idx + r0;
-      nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
+      if constexpr (PAIR) {
+        const int bp = (d.B + 1) >> 1;
+        h = item / bp;
+        qp0 = (item - h * bp) * QT;
+        cols = a.pair_cols + (size_t)item * bp;
+        nt_csr = max(0, min(a.pair_len[item], bp));
+      } else {
+        h = item / d.B;
+        qp0 = (item - h * d.B) * QT;
+        const int r0 = a.row_ptr[item];
+        cols = a.col_idx + r0;
+        nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
+      }
       nt = nt_csr * TPB + (a.patch_only ? 0 : d.ns_pad / KT);
     } else if constexpr (MODE == kDense) {
       h = item / a.q_tiles;
@@ -217,10 +234,19 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     if constexpr (kCsr) {
       const int nb = nt_csr * TPB;
       if (n >= nb) return d.np_pad + min(n - nb, d.ns_pad / KT - 1) * KT;
-      return min(max(raw, 0), d.B - 1) * QT + (n % TPB) * KT;
+      const int last = (PAIR ? (d.B + 1) >> 1 : d.B) - 1;
+      return min(max(raw & 0x0fffffff, 0), last) * QT + (n % TPB) * KT;
     } else {
       return (tile0 + n) * KT;
     }
+  };
+  // Sub-tile activity of this wave in tile n (aligned pairs): bit kh for key
+  // block 2J + kh, i.e. sub-tiles 2 kh, 2 kh + 1; all active otherwise
+  auto tile_act = [&](int n, int raw) -> int {
+    if constexpr (kCsr && PAIR) {
+      if (n < nt_csr * TPB) return (__builtin_amdgcn_readfirstlane(raw) >> (28 + 2 * (w >> 1))) & 3;
+    }
+    return 3;
   };
   auto tile_valid = [&](int kp0) -> int {
     return kp0 < d.np_pad ? min(KT, d.np - kp0) : min(KT, d.ns - (kp0 - d.np_pad));
@@ -343,8 +369,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     l_run *= alpha;
     m_run = m_new;
   };
-  // partial tile, or its exact max (either lane half) more than 64 log2 units
-  // above the running max
+  // partial tile, or its exact max (either lane half) more than kLazySlack
+  // log2 units above the running max
   auto needs_rare = [&](float mx, int valid) -> bool {
     return valid < KT || __any(!(mx * kScaleLog2 - m_run <= kLazySlack));
   };
@@ -378,27 +404,36 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
     issue_k(tile_kp0(n0, raw_cur));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // (aligned pairs: a wave's first tile with any active sub-tile is its
+    // first block)
+    bool fresh = true;
     for (int n = n0; n < n1; ++n) {
       // V^T(n) fills its slot (free since the previous closing barrier) while
       // the scores of tile n run
       const int kp_n = tile_kp0(n, raw_cur);
       issue_v(kp_n);
+      const int act = idle ? 0 : tile_act(n, raw_cur);
       const int raw_after = tile_raw(n + 2);
       f32x16 s[NS];
-      if (!idle) {
+      if (act != 0) {
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
+          if (act & (1 << (2 * t / NS))) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kadr[m] + t * kSubK), qop[m],
-                                                           m == 0 ? f32x16{} : s[t], 0, 0, 0);
-          // a plain chain: the backend folds it into one v_max3 per two scores
+            for (int m = 0; m < 4; ++m)
+              s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(kadr[m] + t * kSubK), qop[m],
+                                                             m == 0 ? f32x16{} : s[t], 0, 0, 0);
+            // a plain chain: the backend folds it into one v_max3 per two scores
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+          } else {
+            s[t] = f32x16{} - INFINITY;  // an inactive sub-tile weighs nothing
+          }
         }
         const int valid = tile_valid(kp_n);
-        if (n == n0 || needs_rare(mx, valid)) rare(s, mx, valid);
+        if (fresh || needs_rare(mx, valid)) rare(s, mx, valid);
+        fresh = false;
       }
       // V^T(n) has landed and every wave is done with K(n): K(n+1) fills the
       // K slot while tile n is exponentiated and multiplied by V^T
@@ -411,7 +446,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
       // MFMAs) from starving the VALU
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < (idle ? 0 : NS); ++t) {
+      for (int t = 0; t < NS; ++t) {
+        if (!(act & (1 << (2 * t / NS)))) continue;
         // the sub-tile's V^T operands are read first and may not be sunk, so
         // the LDS latency hides behind the exponentials
         f16x8 va[2], vb[2];
@@ -578,6 +614,67 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Aligned pairs for b = 64 (see AttnArgs): one wave per pair row (head h,
+// query tile I) ORs the kept blocks of query blocks 2I and 2I + 1 into a
+// 4-bit activity word per key tile J in LDS, then compacts the nonzero words
+// in ascending J with a ballot prefix count.
+__global__ __launch_bounds__(256) void pair_csr_kernel(const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx,
+                                                       Dims d, int32_t* __restrict__ pair_cols,
+                                                       int32_t* __restrict__ pair_len) {
+  extern __shared__ uint32_t acts[];  // [4 waves][bp]
+  const int bp = (d.B + 1) >> 1;
+  const int w = lid_x() >> 6, lane = lid_x() & 63;
+  const int item = wg_x() * 4 + w;
+  const bool live = item < d.H * bp;  // uniform per wave
+  uint32_t* f = acts + w * bp;
+  if (live)
+    for (int j = lane; j < bp; j += 64) f[j] = 0u;
+  __syncthreads();
+  if (live) {
+    const int h = item / bp, i = item - h * bp;
+    for (int hq = 0; hq < 2; ++hq) {
+      const int qb = 2 * i + hq;
+      if (qb >= d.B) break;
+      const int r = h * d.B + qb, a0 = row_ptr[r];
+      const int n = max(0, min(row_ptr[r + 1] - a0, d.B));
+      for (int e = lane; e < n; e += 64) {
+        const int j = col_idx[a0 + e];
+        if (j >= 0 && j < d.B) atomicOr(&f[j >> 1], 1u << (2 * hq + (j & 1)));
+      }
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  int pos = 0;
+  for (int j0 = 0; j0 < bp; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t v = j < bp ? f[j] : 0u;
+    const uint64_t mask = __ballot(v != 0u);
+    if (v != 0u)
+      pair_cols[(size_t)item * bp + pos + __popcll(mask & ((1ull << lane) - 1))] =
+          (int32_t)((uint32_t)j | (v << 28));
+    pos += __popcll(mask);
+  }
+  if (lane == 0) pair_len[item] = pos;
+}
+
+static int pair_rows(const Dims& d) { return (d.B + 1) >> 1; }
+static size_t pair_cols_bytes(const Dims& d) {
+  return ((size_t)d.H * pair_rows(d) * pair_rows(d) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+static size_t pair_len_bytes(const Dims& d) {
+  return ((size_t)d.H * pair_rows(d) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+static hipError_t launch_pair_csr(const Dims& d, const int32_t* row_ptr, const int32_t* col_idx,
+                                  int32_t* pc, int32_t* pl, hipStream_t st) {
+  const int items = d.H * pair_rows(d);
+  pair_csr_kernel<<<(items + 3) / 4, 256, 4 * pair_rows(d) * sizeof(uint32_t), st>>>(
+      row_ptr, col_idx, d, pc, pl);
+  return hipGetLastError();
+}
+
 // Rows that kSparseTail split into pieces: workgroup (XCD x and tail row
 // t < tmax, the largest leftover of any XCD; group g of 4 query rows) merges
 // the row's float32 partials by
@@ -589,7 +686,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          uint16_t* __restrict__ o,
                                                          float* __restrict__ lse, Dims d,
                                                          int rows, int rows_per_xcd, int m,
-                                                         int pieces, int tmax) {
+                                                         int pieces, int tmax, int rows_per_head) {
   constexpr int QT = 128;
   const int x = wg_x() / tmax, t = wg_x() % tmax;
   const int r0 = x * rows_per_xcd;
@@ -620,8 +717,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
     acc += oi[pc] * wgt;
     l += li[pc] * wgt;
   }
-  const int h = item / d.B;
-  const int tok = packed_token((item - h * d.B) * QT + qr, d);
+  const int h = item / rows_per_head;
+  const int tok = packed_token((item - h * rows_per_head) * QT + qr, d);
   if (tok < 0) return;
   o[((size_t)h * d.n + tok) * kHeadDim + dim] =
       __builtin_bit_cast(uint16_t, (__bf16)(l > 0.f ? acc / l : 0.f));
@@ -640,15 +737,11 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
 // with an absolute error under 2^-39 of the maximum.  sigma_h is clamped to
 // [-100, 100] (and 0 for a head without finite nonzero values).
 //
-// vmax_kernel: per (head, chunk of tokens) the largest |V| as bf16 bits
+// vmax_kernel: per (head, chunk of tokens) the largest |x| as bf16 bits
 // (the sign cleared, non-negative bf16 values order like their bit
-// patterns); pack_kernel reduces the head's chunks, derives sigma_h, and
-// writes it once per head.
-constexpr int kVmaxChunks = 64;
-
-static int vmax_chunks(const Dims& d) { return min(kVmaxChunks, (d.n + 1023) / 1024); }
-
-__global__ __launch_bounds__(256) void vmax_kernel(const uint4* __restrict__ v,
+// patterns); pack_kernel reduces the head's chunks (head_sigma), derives
+// sigma_h, and writes it once per head.
+static __global__ __launch_bounds__(256) void vmax_kernel(const uint4* __restrict__ v,
                                                    uint32_t* __restrict__ chunk_max, Dims d,
                                                    int nchunk) {
   const int c = wg_x(), h = wg_y(), T = lid_x();
@@ -667,14 +760,7 @@ __global__ __launch_bounds__(256) void vmax_kernel(const uint4* __restrict__ v,
   __shared__ uint32_t red[4];
   if ((T & 63) == 0) red[T >> 6] = m;
   __syncthreads();
-  if (T == 0) chunk_max[h * kVmaxChunks + c] = max(max(red[0], red[1]), max(red[2], red[3]));
-}
-
-// sigma_h from the largest |V| (bf16 bits of the absolute value)
-__device__ inline int v_sigma(uint32_t mb) {
-  if (mb == 0 || mb >= 0x7f80u) return 0;  // all zero, or inf / NaN present
-  const int e = (int)(mb >> 7) - 127;      // |V| max in [2^e, 2^(e+1)) (e = -127: subnormal)
-  return min(100, max(-100, 14 - e));
+  if (T == 0) chunk_max[h * kAbsmaxChunks + c] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
@@ -687,12 +773,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ k,
   __shared__ int sig_s;
   const int kp0 = wg_x() * 64, h = wg_y(), T = lid_x();
   if (T < 64) {
-    uint32_t m = T < nchunk ? chunk_max[h * kVmaxChunks + T] : 0u;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    const int sig = head_sigma(chunk_max, h, nchunk, T);
     if (T == 0) {
-      sig_s = v_sigma(m);
-      if (wg_x() == 0) vsig[h] = sig_s;
+      sig_s = sig;
+      if (wg_x() == 0) vsig[h] = sig;
     }
   }
   const size_t src_head = (size_t)h * d.n * 8;
@@ -755,15 +839,20 @@ static uint32_t* packed_chunk_max(const Dims& d, const uint16_t* kp) {
 
 size_t pack_bytes(const Dims& d) {
   return pack_kv_bytes(d) + align256((size_t)d.H * sizeof(int)) +
-         align256((size_t)d.H * kVmaxChunks * sizeof(uint32_t));
+         align256((size_t)d.H * kAbsmaxChunks * sizeof(uint32_t));
+}
+
+hipError_t launch_absmax(const Dims& d, const uint16_t* x, uint32_t* chunk_max, hipStream_t st) {
+  vmax_kernel<<<dim3(absmax_chunks(d), d.H), 256, 0, st>>>((const uint4*)x, chunk_max, d,
+                                                         absmax_chunks(d));
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v, uint16_t* kp,
                        uint16_t* vt, hipStream_t st) {
-  const int nchunk = vmax_chunks(d);
+  const int nchunk = absmax_chunks(d);
   uint32_t* cm = packed_chunk_max(d, kp);
-  vmax_kernel<<<dim3(nchunk, d.H), 256, 0, st>>>((const uint4*)v, cm, d, nchunk);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_absmax(d, v, cm, st);
   if (e != hipSuccess) return e;
   pack_kernel<<<dim3(d.ntot_pad / 64, d.H), 256, 0, st>>>(
       (const uint4*)k, (const uint4*)v, (uint4*)kp, (uint4*)vt, cm, packed_vsig(d, kp), d, nchunk);
@@ -823,10 +912,10 @@ static int device_slots() {
   return 768;
 }
 
-static TailPlan tail_plan(const Dims& d) {
+static TailPlan tail_plan(const Dims& d, int rows_per_head) {
   TailPlan p;
   p.m = device_slots() / kXcds;
-  p.rows = d.H * d.B;
+  p.rows = d.H * rows_per_head;
   p.rows_per_xcd = (p.rows + kXcds - 1) / kXcds;
   p.pieces = 0;
   p.slots = 0;
@@ -849,7 +938,8 @@ static TailPlan tail_plan(const Dims& d) {
   } else {
     double best = 0.8;
     for (int pc = 2; pc <= kMaxTailPieces; ++pc) {
-      const double cost = (double)((max_rem * pc + p.m - 1) / p.m) / pc + (double)pc / (d.B + 1);
+      const double cost =
+          (double)((max_rem * pc + p.m - 1) / p.m) / pc + (double)pc / (rows_per_head + 1);
       if (cost < best) {
         best = cost;
         p.pieces = pc;
@@ -871,10 +961,38 @@ static size_t tail_part_o_bytes(const TailPlan& p) {
   return ((size_t)p.slots * 128 * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
 }
 
-size_t patch_rows_workspace(const Dims& d) {
-  if (d.b != 128) return 0;
-  const TailPlan p = tail_plan(d);
+// Workspace of the patch-row call.  b = 128: the split last round (pieces'
+// float32 partials).  b = 64: the aligned-pair lists, then the split last
+// round of the pair rows.
+static size_t tail_bytes(const TailPlan& p) {
   return tail_part_o_bytes(p) + (size_t)p.slots * 128 * 2 * sizeof(float);
+}
+size_t patch_rows_workspace(const Dims& d) {
+  if (d.b == 128) return tail_bytes(tail_plan(d, d.B));
+  return pair_cols_bytes(d) + pair_len_bytes(d) + tail_bytes(tail_plan(d, pair_rows(d)));
+}
+
+template <bool PAIR>
+static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, void* tail_ws,
+                                  size_t tail_ws_bytes, hipStream_t st) {
+  a.n_items = d.H * rows_per_head;
+  const TailPlan p = tail_plan(d, rows_per_head);
+  if (tail_ws != nullptr && p.slots > 0 && tail_ws_bytes >= tail_bytes(p)) {
+    a.part_o = (float*)tail_ws;
+    a.part_ml = (float*)((char*)tail_ws + tail_part_o_bytes(p));
+    a.rows_per_xcd = p.rows_per_xcd;
+    a.tail_m = p.m;
+    a.tail_pieces = p.pieces;
+    attn_kernel<128, 128, kSparseTail, 3, PAIR><<<kXcds * p.grid, 256, 0, st>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
+        a.part_o, a.part_ml, a.o, a.lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem,
+        rows_per_head);
+    return hipGetLastError();
+  }
+  attn_kernel<128, 128, kSparseFused, 3, PAIR><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
@@ -884,21 +1002,16 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
-  if (d.b == 128 && ws != nullptr) {
-    const TailPlan p = tail_plan(d);
-    if (p.slots > 0 && ws_bytes >= tail_part_o_bytes(p) + (size_t)p.slots * 128 * 2 * sizeof(float)) {
-      a.part_o = (float*)ws;
-      a.part_ml = (float*)((char*)ws + tail_part_o_bytes(p));
-      a.rows_per_xcd = p.rows_per_xcd;
-      a.tail_m = p.m;
-      a.tail_pieces = p.pieces;
-      attn_kernel<128, 128, kSparseTail, 3><<<kXcds * p.grid, 256, 0, st>>>(a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
-          a.part_o, a.part_ml, o, lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem);
-      return hipGetLastError();
-    }
+  if (ws != nullptr && d.b == 128) return launch_rows_128<false>(d, a, d.B, ws, ws_bytes, st);
+  if (ws != nullptr && d.b == 64 && ws_bytes >= pair_cols_bytes(d) + pair_len_bytes(d)) {
+    int32_t* pc = (int32_t*)ws;
+    int32_t* pl = (int32_t*)((char*)ws + pair_cols_bytes(d));
+    const hipError_t e = launch_pair_csr(d, row_ptr, col_idx, pc, pl, st);
+    if (e != hipSuccess) return e;
+    a.pair_cols = pc;
+    a.pair_len = pl;
+    const size_t used = pair_cols_bytes(d) + pair_len_bytes(d);
+    return launch_rows_128<true>(d, a, pair_rows(d), (char*)ws + used, ws_bytes - used, st);
   }
   return run_attn_b<kSparseFused>(d, a, st);
 }

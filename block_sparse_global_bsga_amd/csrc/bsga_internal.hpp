@@ -105,7 +105,37 @@ __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
+// Power-of-two operand scales.  An operand headed for a float16 MFMA operand
+// is stored as x * 2^sigma, with sigma chosen per head from the head's
+// largest |x| (bf16 bits with the sign cleared, mb) so that it lies in
+// [2^14, 2^15): every bf16 value is then exact in float16 except those more
+// than 2^28 below the maximum (float16 subnormals, absolute error under 2^-39
+// of it).  sigma is clamped to [-100, 100]; 0 when the head has no finite
+// nonzero value.  The maxima come per chunk of tokens (at most
+// kAbsmaxChunks chunks per head) from launch_absmax.
+constexpr int kAbsmaxChunks = 64;
+inline int absmax_chunks(const Dims& d) {
+  const int c = (d.n + 1023) / 1024;
+  return c < kAbsmaxChunks ? c : kAbsmaxChunks;
+}
+__device__ inline int sigma_of_max(uint32_t mb) {
+  if (mb == 0 || mb >= 0x7f80u) return 0;  // all zero, or inf / NaN present
+  const int e = (int)(mb >> 7) - 127;      // max in [2^e, 2^(e+1)) (e = -127: subnormal)
+  return min(100, max(-100, 14 - e));
+}
+// the largest |x| of head h from its chunk maxima, reduced by the 64 lanes
+// of a wave (lane = the calling lane), as sigma
+__device__ inline int head_sigma(const uint32_t* chunk_max, int h, int nchunk, int lane) {
+  uint32_t m = lane < nchunk ? chunk_max[h * kAbsmaxChunks + lane] : 0u;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  return sigma_of_max(m);
+}
+
 // ---------------------------------------------------------------- launchers
+// per (head, chunk) largest |x| of a [H][N][64] bf16 tensor, as bf16 bits,
+// into chunk_max[H][kAbsmaxChunks]
+hipError_t launch_absmax(const Dims& d, const uint16_t* x, uint32_t* chunk_max, hipStream_t st);
 // Each returns hipSuccess or the launch error.  All pointers are device
 // pointers validated by the caller.
 hipError_t launch_pool(const Dims& d, const uint16_t* q, const uint16_t* k,

@@ -325,9 +325,15 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
  *     merge in bsga_special_dense, without the intermediate bf16 rounding).
  *     Optional workspace (NULL, or bsga_workspace_bytes(
- *     BSGA_OP_PATCH_ROWS_PACKED) bytes: 0 for b = 64, and 0 when splitting
- *     would not shorten the last round): with it, at b = 128 the query
- *     blocks left for the last, partial round of workgroups are split into
+ *     BSGA_OP_PATCH_ROWS_PACKED) bytes; at b = 128 it is 0 when splitting
+ *     would not shorten the last round).  At b = 64 a workspace lets the
+ *     call run query blocks in aligned pairs: query blocks 2I, 2I + 1 form a
+ *     128-query tile that walks the 128-key tiles (key blocks 2J, 2J + 1)
+ *     holding a block either of them keeps, each wave skipping the 32-key
+ *     sub-tiles its query block does not keep (the same softmax; the lists
+ *     are built on the device into the workspace); without one, 64-query
+ *     tiles walk 64-key tiles.  With it, at b = 128 (and for the pairs) the
+ *     query blocks left for the last, partial round of workgroups are split into
  *     pieces of consecutive key tiles (as many per block as let them all run
  *     at once when that round is at most half full; for a fuller round the
  *     count, at most 16, whose pieces finish first, if that is under 0.8 of

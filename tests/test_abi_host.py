@@ -105,7 +105,22 @@ def test_capacity_and_workspace_sizes():
     assert tail_bytes(5488, 343) == 8 * 14 * 6 * 128 * 66 * 4
     assert tail_bytes(5488, 343) <= tail <= tail_bytes(5488, 343) + 512
     assert bsga.workspace_bytes(shape, bsga.OP_LAYER) >= tail
-    assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    # patch rows at b = 64: the aligned-pair lists (a key-tile list of up to
+    # ceil(B / 2) entries and its length per pair of query blocks), then the
+    # split last round of the pair rows.  The 8-frame layer: B = 172, 86 pair
+    # rows per head, 1376 rows, 172 per XCD, 76 in the last round of 96
+    # slots: no piece count shortens it
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    pairs = up(16 * 86 * 86 * 4) + up(16 * 86 * 4)
+    assert tail_bytes(1376, 86) == 0
+    assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) == pairs
+    # the four-frame layer: B = 16, 8 pair rows per head, 32 rows (4 heads),
+    # 4 per XCD, split into 96 // 4 = 24 -> 16 pieces each
+    pairs = up(4 * 8 * 8 * 4) + up(4 * 8 * 4)
+    assert tail_bytes(32, 8) == 8 * 4 * 16 * 128 * 66 * 4
+    assert pairs + tail_bytes(32, 8) <= bsga.workspace_bytes(S(4, 256, 5, 4, 64),
+                                                          bsga.OP_PATCH_ROWS_PACKED) \
+        <= pairs + tail_bytes(32, 8) + 512
     # 400 rows (16 heads x 25 blocks): 50 per XCD, more than half a round: 3
     # pieces each, in two rounds of a third of a row
     assert tail_pieces(50, 25) == 3 and tail_bytes(400, 25) == 8 * 50 * 3 * 128 * 66 * 4
