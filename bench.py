@@ -71,9 +71,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(workload):
     """HBM bytes per launch of the patch-row kernel from the committed counter
-    summary, or None when that summary was taken on different kernel sources."""
+    summary, or None when that summary was taken on different kernel sources
+    or on another workload."""
     try:
         fields = {}
         with open(TRAFFIC_FILE) as f:
@@ -82,6 +83,8 @@ def recorded_traffic():
                     key, val = line.split(":", 1)
                     fields[key.strip()] = val.strip()
         if fields.get("kernel_source_sha256") != kernel_source_digest():
+            return None
+        if fields.get("workload") != workload:
             return None
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -479,11 +482,13 @@ def main():
         "layer_frac_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "density": round(density, 4),
         "roofline": {"bound": "mfma",
-                     "kernel": "attn_kernel<128, 128, kSparseTail> + tail_merge_kernel "
-                               "(bsga_patch_rows_packed)",
+                     "kernel": ("attn_kernel<128, 128, kSparseTail> + tail_merge_kernel "
+                                "(bsga_patch_rows_packed)" if cfg.block == 128 else
+                                "pair_csr_kernel + attn_kernel<128, 128, PAIR> over aligned "
+                                "pairs of 64-blocks (bsga_patch_rows_packed)"),
                      "achieved": round(kern_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-                     "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic()},
+                     "kernel_ms": round(kern_ms, 4), "traffic": recorded_traffic(cfg.name)},
         "stages": stages_out,
         "cpu_baseline": cpu,
         **extras,

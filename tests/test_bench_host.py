@@ -77,12 +77,24 @@ def test_traffic_figure_only_for_its_sources(tmp_path, monkeypatch):
     path = tmp_path / "traffic.txt"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     digest = bench.kernel_source_digest()
-    path.write_text(f"# comment: ignored\nkernel_source_sha256: {digest}\n"
+    w = "vggt-32f-518-h16-b128"
+    path.write_text(f"# comment: ignored\nworkload: {w}\nkernel_source_sha256: {digest}\n"
                     "hbm_bytes_per_launch: 2156610572\n")
-    assert bench.recorded_traffic() == 2156610572.0
-    path.write_text("kernel_source_sha256: " + "0" * 64 + "\nhbm_bytes_per_launch: 5\n")
-    assert bench.recorded_traffic() is None
-    path.write_text(f"kernel_source_sha256: {digest}\n")
-    assert bench.recorded_traffic() is None
+    assert bench.recorded_traffic(w) == 2156610572.0
+    # measured on another workload: not this one's figure
+    assert bench.recorded_traffic("vggt-8f-518-h16-b64") is None
+    path.write_text(f"workload: {w}\nkernel_source_sha256: " + "0" * 64 +
+                    "\nhbm_bytes_per_launch: 5\n")
+    assert bench.recorded_traffic(w) is None
+    path.write_text(f"workload: {w}\nkernel_source_sha256: {digest}\n")
+    assert bench.recorded_traffic(w) is None
+    path.write_text(f"kernel_source_sha256: {digest}\nhbm_bytes_per_launch: 5\n")
+    assert bench.recorded_traffic(w) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
-    assert bench.recorded_traffic() is None
+    assert bench.recorded_traffic(w) is None
+    # the committed summary names the default workload
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", os.path.join(ROOT, "profiles",
+                                                            "attn_patch_rows_32f_hbm_traffic.txt"))
+    from block_sparse_global_bsga_amd import synth
+    text = open(bench.TRAFFIC_FILE).read()
+    assert f"workload: {synth.CONFIGS[3].name}" in text
