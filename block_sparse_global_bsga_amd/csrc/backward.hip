@@ -22,7 +22,13 @@
 // dkdv_kernel (key-major, over the transposed CSR): per wave 32 keys with K
 //   and V rows in registers; per query tile S = Q K^T and dP = dO V^T (Q, dO
 //   rows from LDS, row permutation pi), then dV^T += dO^T P and
-//   dK^T += Q^T dS from the accumulators.
+//   dK^T += Q^T dS from the accumulators.  There P carries a factor 2^15
+//   (exp2 against LSE - 15) so that every weight that matters is a normal
+//   float16 number, and dV^T += dO^T P runs on float16 MFMA with dO^T stored
+//   as float16 times a per-head power of two 2^sigma (its largest |dO| in
+//   [2^14, 2^15)): P enters once, rounded to 11 significant bits, while dS
+//   still enters dK as a bf16 pair hi + lo.  The epilogue undoes 2^15 (dK)
+//   and 2^(15 + sigma) (dV).
 #include <type_traits>
 
 #include "bsga_internal.hpp"
@@ -33,31 +39,62 @@ namespace bsga {
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// dkdv_kernel's weights are 2^kPScaleLog2 P: every weight above 2^-29 is a
+// normal float16 number, and none exceeds 2^15
+constexpr float kPScaleLog2 = 15.f;
+
 // ---------------------------------------------------------------------------
 // Packing: rows and/or transposed copies of one [H][N][64] tensor in packed
 // order, 64 tokens per workgroup (zeros for padding).
+// With chunk_max given, the transposed copy holds float16 x * 2^sigma_h
+// (sigma_h from the head's largest |x|, written to sig[h]) instead of bf16.
 __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint4* __restrict__ x,
                                                        uint4* __restrict__ rows,
-                                                       uint4* __restrict__ cols, Dims d) {
+                                                       uint4* __restrict__ cols, Dims d,
+                                                       const uint32_t* __restrict__ chunk_max,
+                                                       int* __restrict__ sig, int nchunk) {
   __shared__ uint16_t sv[64][66];
+  __shared__ int sig_s;
   const int kp0 = wg_x() * 64, h = wg_y(), T = lid_x();
+  if (chunk_max != nullptr && T < 64) {
+    const int sg = head_sigma(chunk_max, h, nchunk, T);
+    if (T == 0) {
+      sig_s = sg;
+      if (wg_x() == 0) sig[h] = sg;
+    }
+  }
   const size_t src_head = (size_t)h * d.n * 8;
+  uint4 vv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = T + 256 * i;
     const int row = c >> 3, ch = c & 7;
     const int tok = packed_token(kp0 + row, d);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (tok >= 0) v = x[src_head + (size_t)tok * 8 + ch];
-    if (rows) rows[((size_t)h * d.ntot_pad + kp0 + row) * 8 + ch] = v;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[row][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xffff);
-      sv[row][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
+    vv[i] = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) vv[i] = x[src_head + (size_t)tok * 8 + ch];
+    if (rows) rows[((size_t)h * d.ntot_pad + kp0 + row) * 8 + ch] = vv[i];
   }
   if (!cols) return;
+  __syncthreads();  // sig_s
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = T + 256 * i;
+    const int row = c >> 3, ch = c & 7;
+    const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t lo = (uint16_t)(w[e] & 0xffff), hi = (uint16_t)(w[e] >> 16);
+      if (chunk_max != nullptr) {
+        // bf16 -> float32 (exact) -> times 2^sigma (exact) -> float16 (exact in range)
+        lo = __builtin_bit_cast(uint16_t,
+                                (_Float16)__builtin_amdgcn_ldexpf(__uint_as_float(w[e] << 16), sig_s));
+        hi = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(
+                                              __uint_as_float(w[e] & 0xffff0000u), sig_s));
+      }
+      sv[row][ch * 8 + 2 * e] = lo;
+      sv[row][ch * 8 + 2 * e + 1] = hi;
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -72,13 +109,15 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint4* __restrict__
 }
 
 // Per packed row: lse2 = LSE * log2(e) (+inf for padding, so every weight of
-// a padding row is 0) and D = dO . O in float32 (0 for padding).  dq_kernel
-// overwrites D for every row of its query tiles with sum_k P dP; rows no
-// query tile covers are padding and keep 0.
+// a padding row is 0), lse2s = lse2 - 15 (the weights 2^15 P of dkdv_kernel)
+// and D = dO . O in float32 (0 for padding).  dq_kernel overwrites D for
+// every row of its query tiles with sum_k P dP; rows no query tile covers
+// are padding and keep 0.
 __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restrict__ o,
                                                            const uint4* __restrict__ d_o,
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ lse2,
+                                                           float* __restrict__ lse2s,
                                                            float* __restrict__ dd, Dims d) {
   const int h = wg_y(), T = lid_x(), ch = T & 7;
   const int kp = wg_x() * 32 + (T >> 3);  // 32 rows per workgroup, 8 lanes per row
@@ -100,7 +139,9 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restri
   if (ch == 0) {
     const size_t r = (size_t)h * d.ntot_pad + kp;
     dd[r] = s;
-    lse2[r] = tok >= 0 ? lse[(size_t)h * d.n + tok] * 1.4426950408889634f : INFINITY;
+    const float l2 = tok >= 0 ? lse[(size_t)h * d.n + tok] * 1.4426950408889634f : INFINITY;
+    lse2[r] = l2;
+    lse2s[r] = l2 - kPScaleLog2;
   }
 }
 
@@ -243,6 +284,9 @@ constexpr uint32_t kHalfCols = 32 * 8 * 16;  // 32 dims of a transposed 64-token
 __device__ inline bf16x8 lds_op(const u32x4* smem, uint32_t off) {
   return as_bf16x8(*(const u32x4*)((const char*)smem + off));
 }
+__device__ inline f16x8 lds_op16(const u32x4* smem, uint32_t off) {
+  return __builtin_bit_cast(f16x8, *(const u32x4*)((const char*)smem + off));
+}
 // Score r of a lane's 32-row sub-tile accumulator is row pi(8 (r / 4) + 4 hh
 // + r % 4) = kc(r) + 8 hh of the sub-tile.
 __device__ constexpr int acc_row(int r) { return 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3); }
@@ -256,6 +300,8 @@ struct BwdArgs {
   const uint16_t* kt;
   const uint16_t* vp;
   const float* lse2;    // [H][Ntot]
+  const float* lse2s;   // [H][Ntot] lse2 - kPScaleLog2, read by dkdv_kernel
+  const int* dosig;     // [H] sigma of the float16 dO^T copy
   const float* dd;      // [H][Ntot] D per packed row, read by dkdv_kernel
   float* dd_out;        // the same array, written by dq_kernel
   const int32_t* row_ptr;
@@ -521,7 +567,7 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
     // lse2 and D of the tile's 64 queries: one 4-byte direct-to-LDS load per
     // lane, issued by waves 0 and 1 (no register round trip, no extra wait)
     if (w < 2)
-      __builtin_amdgcn_global_load_lds((const void*)((w == 0 ? a.lse2 : a.dd) + hrow + qp0 + lane),
+      __builtin_amdgcn_global_load_lds((const void*)((w == 0 ? a.lse2s : a.dd) + hrow + qp0 + lane),
                                        (lds_void*)&stats[slot][w][0], 4, 0, 0);
   };
 
@@ -562,27 +608,22 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
             p8[e] = p;
             s8[e] = p * (dp[r] - dd_t[qq]);
           }
-          // P and dS enter the products as bf16 pairs hi + lo: dV and dK of a
-          // key sum thousands of weighted rows, and a single bf16 rounding of
-          // each weight would dominate their error
-          const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+          // P enters dV once as float16 (11 significant bits; a bf16
+          // rounding of each weight would dominate the error of a key that
+          // sums thousands of weighted rows), dS enters dK as a bf16 pair
+          // hi + lo (dS is a small difference of large terms)
+          const f16x8 pf = __builtin_convertvector(p8, f16x8);
           const bf16x8 sb = __builtin_convertvector(s8, bf16x8);
-          f32x8 prem, rem;
+          f32x8 rem;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            prem[e] = p8[e] - (float)pb[e];
-            rem[e] = s8[e] - (float)sb[e];
-          }
-          const bf16x8 pl = __builtin_convertvector(prem, bf16x8);
+          for (int e = 0; e < 8; ++e) rem[e] = s8[e] - (float)sb[e];
           const bf16x8 sl = __builtin_convertvector(rem, bf16x8);
-          const bf16x8 o0 = lds_op(smem, otb + op.col[t][h2]);
-          const bf16x8 o1 = lds_op(smem, otb + op.col[t][h2] + kHalfCols);
+          const f16x8 o0 = lds_op16(smem, otb + op.col[t][h2]);
+          const f16x8 o1 = lds_op16(smem, otb + op.col[t][h2] + kHalfCols);
           const bf16x8 q0 = lds_op(smem, qtb + op.col[t][h2]);
           const bf16x8 q1 = lds_op(smem, qtb + op.col[t][h2] + kHalfCols);
-          v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pb, v0, 0, 0, 0);
-          v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pb, v1, 0, 0, 0);
-          v0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, pl, v0, 0, 0, 0);
-          v1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, pl, v1, 0, 0, 0);
+          v0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(o0, pf, v0, 0, 0, 0);
+          v1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(o1, pf, v1, 0, 0, 0);
           k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sb, k0, 0, 0, 0);
           k1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1, sb, k1, 0, 0, 0);
           k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sl, k0, 0, 0, 0);
@@ -605,15 +646,19 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
   if (tok < 0) return;
   float* ok = a.dk + ((size_t)h * d.n + tok) * kHeadDim;
   float* ov = a.dv + ((size_t)h * d.n + tok) * kHeadDim;
+  // exact powers of two: 1/8 and 2^-15 for dK, 2^-(15 + sigma) for dV
+  const float ks = __builtin_amdgcn_ldexpf(0.125f, -(int)kPScaleLog2);
+  const float vs = __builtin_amdgcn_ldexpf(1.f, -(int)kPScaleLog2 - a.dosig[h]);
 #pragma unroll
   for (int aa = 0; aa < 4; ++aa) {
     *(f32x4*)(ok + 8 * aa + 4 * hh) =
-        f32x4{k0[4 * aa], k0[4 * aa + 1], k0[4 * aa + 2], k0[4 * aa + 3]} * 0.125f;
+        f32x4{k0[4 * aa], k0[4 * aa + 1], k0[4 * aa + 2], k0[4 * aa + 3]} * ks;
     *(f32x4*)(ok + 32 + 8 * aa + 4 * hh) =
-        f32x4{k1[4 * aa], k1[4 * aa + 1], k1[4 * aa + 2], k1[4 * aa + 3]} * 0.125f;
-    *(f32x4*)(ov + 8 * aa + 4 * hh) = f32x4{v0[4 * aa], v0[4 * aa + 1], v0[4 * aa + 2], v0[4 * aa + 3]};
+        f32x4{k1[4 * aa], k1[4 * aa + 1], k1[4 * aa + 2], k1[4 * aa + 3]} * ks;
+    *(f32x4*)(ov + 8 * aa + 4 * hh) =
+        f32x4{v0[4 * aa], v0[4 * aa + 1], v0[4 * aa + 2], v0[4 * aa + 3]} * vs;
     *(f32x4*)(ov + 32 + 8 * aa + 4 * hh) =
-        f32x4{v1[4 * aa], v1[4 * aa + 1], v1[4 * aa + 2], v1[4 * aa + 3]};
+        f32x4{v1[4 * aa], v1[4 * aa + 1], v1[4 * aa + 2], v1[4 * aa + 3]} * vs;
   }
 }
 
@@ -621,7 +666,9 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
 size_t backward_workspace(const Dims& d) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t arr = up((size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t));
-  return 7 * arr + 2 * up((size_t)d.H * d.ntot_pad * sizeof(float)) +
+  return 7 * arr + 3 * up((size_t)d.H * d.ntot_pad * sizeof(float)) +
+         up((size_t)d.H * kAbsmaxChunks * sizeof(uint32_t)) +  // dO chunk maxima
+         up((size_t)d.H * sizeof(int)) +                      // dO sigma
          up(((size_t)d.H * d.B + 1) * sizeof(int32_t)) +   // t_ptr
          up((size_t)d.H * d.B * sizeof(int32_t)) +         // counts
          up((size_t)d.H * d.B * d.B * sizeof(int32_t));   // t_list
@@ -644,26 +691,36 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
   uint16_t* kt = (uint16_t*)p; p += arr;
   uint16_t* vp = (uint16_t*)p; p += arr;
   float* lse2 = (float*)p; p += up((size_t)d.H * d.ntot_pad * sizeof(float));
+  float* lse2s = (float*)p; p += up((size_t)d.H * d.ntot_pad * sizeof(float));
   float* dd = (float*)p; p += up((size_t)d.H * d.ntot_pad * sizeof(float));
+  uint32_t* do_max = (uint32_t*)p; p += up((size_t)d.H * kAbsmaxChunks * sizeof(uint32_t));
+  int* dosig = (int*)p; p += up((size_t)d.H * sizeof(int));
   int32_t* t_ptr = (int32_t*)p; p += up(((size_t)d.H * d.B + 1) * sizeof(int32_t));
   int32_t* counts = (int32_t*)p; p += up((size_t)d.H * d.B * sizeof(int32_t));
   int32_t* t_list = (int32_t*)p;
 
   const dim3 pg(d.ntot_pad / 64, d.H);
-  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)q, (uint4*)qp, (uint4*)qt, d);
-  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)d_o, (uint4*)dop, (uint4*)dot, d);
-  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)k, (uint4*)kp, (uint4*)kt, d);
-  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)v, (uint4*)vp, nullptr, d);
+  const int nchunk = absmax_chunks(d);
+  hipError_t e = launch_absmax(d, d_o, do_max, st);
+  if (e != hipSuccess) return e;
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)q, (uint4*)qp, (uint4*)qt, d, nullptr,
+                                      nullptr, 0);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)d_o, (uint4*)dop, (uint4*)dot, d, do_max,
+                                      dosig, nchunk);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)k, (uint4*)kp, (uint4*)kt, d, nullptr,
+                                      nullptr, 0);
+  bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)v, (uint4*)vp, nullptr, d, nullptr, nullptr,
+                                      0);
   bwd_rowstats_kernel<<<dim3(d.ntot_pad / 32, d.H), 256, 0, st>>>(
-      (const uint4*)o, (const uint4*)d_o, lse, lse2, dd, d);
+      (const uint4*)o, (const uint4*)d_o, lse, lse2, lse2s, dd, d);
   csr_t_count_kernel<<<dim3(d.B, d.H), 256, 0, st>>>(row_ptr, col_idx, d, counts);
-  hipError_t e = launch_scan_counts(counts, d.H * d.B, t_ptr, st);
+  e = launch_scan_counts(counts, d.H * d.B, t_ptr, st);
   if (e != hipSuccess) return e;
   csr_t_fill_kernel<<<dim3(d.B, d.H), 256, 0, st>>>(row_ptr, col_idx, t_ptr, d, t_list);
 
   BwdArgs a = {};
   a.qp = qp; a.qt = qt; a.dop = dop; a.dot = dot; a.kp = kp; a.kt = kt; a.vp = vp;
-  a.lse2 = lse2; a.dd = dd; a.dd_out = dd; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.lse2 = lse2; a.lse2s = lse2s; a.dosig = dosig; a.dd = dd; a.dd_out = dd; a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.t_ptr = t_ptr; a.t_list = t_list; a.dq = dq; a.dk = dk; a.dv = dv; a.d = d;
   if (d.b == 128) {
     a.n_items = d.H * (d.B + d.ns_pad / 128);

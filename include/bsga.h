@@ -268,9 +268,12 @@ int bsga_nmse(const bsga_shape* shape, const uint16_t* o_ref, const uint16_t* o,
  *   dq, dk, dv: [H][N][64] float32 outputs, 16-byte aligned, fully written.
  *   workspace: bsga_workspace_bytes(BSGA_OP_BACKWARD) (packed operands,
  *     row statistics and the transposed mask).
- * bf16 MFMA products with float32 accumulation; P and dS enter them as bf16
- * pairs hi + lo, and D = dO . O is recomputed as sum_k P dP from the same
- * float32 P and dP (the stored bf16 O is not used for it).  No atomics: dQ
+ * MFMA products with float32 accumulation: S, dP and the dQ, dK products in
+ * bf16, with dS entering as a bf16 pair hi + lo; dV = P^T dO in float16, with
+ * P (times 2^15) rounded once to float16 and dO times a per-head power of two
+ * (exact for bf16 values), so each weight of dV carries a relative rounding of
+ * at most 2^-11.  D = dO . O is recomputed as sum_k P dP from the same float32
+ * P and dP (the stored bf16 O is not used for it).  No atomics: dQ
  * is accumulated per query tile over the mask's rows, dK and dV per key tile
  * over its transpose (deterministic). */
 int bsga_attn_backward(const bsga_shape* shape, const uint16_t* q,
