@@ -661,6 +661,9 @@ __global__ __launch_bounds__(256) void pair_csr_kernel(const int32_t* __restrict
 }
 
 static int pair_rows(const Dims& d) { return (d.B + 1) >> 1; }
+// pair_csr_kernel keeps four rows of activity words in LDS (64 KB at most)
+constexpr int kMaxPairRows = 4096;
+static bool pairable(const Dims& d) { return d.b == 64 && pair_rows(d) <= kMaxPairRows; }
 static size_t pair_cols_bytes(const Dims& d) {
   return ((size_t)d.H * pair_rows(d) * pair_rows(d) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
@@ -969,6 +972,7 @@ static size_t tail_bytes(const TailPlan& p) {
 }
 size_t patch_rows_workspace(const Dims& d) {
   if (d.b == 128) return tail_bytes(tail_plan(d, d.B));
+  if (!pairable(d)) return 0;  // the unpaired 64-row kernel needs none
   return pair_cols_bytes(d) + pair_len_bytes(d) + tail_bytes(tail_plan(d, pair_rows(d)));
 }
 
@@ -1003,7 +1007,7 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
   if (ws != nullptr && d.b == 128) return launch_rows_128<false>(d, a, d.B, ws, ws_bytes, st);
-  if (ws != nullptr && d.b == 64 && ws_bytes >= pair_cols_bytes(d) + pair_len_bytes(d)) {
+  if (ws != nullptr && pairable(d) && ws_bytes >= pair_cols_bytes(d) + pair_len_bytes(d)) {
     int32_t* pc = (int32_t*)ws;
     int32_t* pl = (int32_t*)((char*)ws + pair_cols_bytes(d));
     const hipError_t e = launch_pair_csr(d, row_ptr, col_idx, pc, pl, st);

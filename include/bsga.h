@@ -329,8 +329,9 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     merge in bsga_special_dense, without the intermediate bf16 rounding).
  *     Optional workspace (NULL, or bsga_workspace_bytes(
  *     BSGA_OP_PATCH_ROWS_PACKED) bytes; at b = 128 it is 0 when splitting
- *     would not shorten the last round).  At b = 64 a workspace lets the
- *     call run query blocks in aligned pairs: query blocks 2I, 2I + 1 form a
+ *     would not shorten the last round; at b = 64 it is 0 when B > 8192).
+ *     At b = 64 (B <= 8192) a workspace lets the call run query blocks in
+ *     aligned pairs: query blocks 2I, 2I + 1 form a
  *     128-query tile that walks the 128-key tiles (key blocks 2J, 2J + 1)
  *     holding a block either of them keeps, each wave skipping the 32-key
  *     sub-tiles its query block does not keep (the same softmax; the lists

@@ -114,6 +114,10 @@ def test_capacity_and_workspace_sizes():
     pairs = up(16 * 86 * 86 * 4) + up(16 * 86 * 4)
     assert tail_bytes(1376, 86) == 0
     assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) == pairs
+    # past 4096 pair rows (B > 8192) the pair lists' LDS would not fit: the
+    # call keeps the unpaired 64-row kernel, which needs no workspace
+    assert bsga.workspace_bytes(S(400, 1369, 5, 2, 64), bsga.OP_PATCH_ROWS_PACKED) == 0
+    assert bsga.workspace_bytes(S(382, 1369, 5, 2, 64), bsga.OP_PATCH_ROWS_PACKED) > 0
     # the four-frame layer: B = 16, 8 pair rows per head, 32 rows (4 heads),
     # 4 per XCD, split into 96 // 4 = 24 -> 16 pieces each
     pairs = up(4 * 8 * 8 * 4) + up(4 * 8 * 4)
