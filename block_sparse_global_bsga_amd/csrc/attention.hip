@@ -75,7 +75,11 @@ namespace bsga {
 //                of consecutive key tiles, listed piece-major after the XCD's
 //                whole rows: the in-order dispatch then spreads that round
 //                over every slot, and concurrent pieces read the same key range
-//                of consecutive rows; tail_merge_kernel combines the pieces
+//                of consecutive rows; tail_merge_kernel combines the pieces.
+//                Given a workspace (B <= 4096), each head's query blocks are
+//                worked longest kept list first (row_order_kernel), so that
+//                the workgroups an XCD runs at once hold rows of similar
+//                length and the last round holds the shortest ones
 enum Mode { kDense = 1, kSpecialSplit = 2, kPatchSpecial = 3, kSparseFused = 4, kSparseTail = 5 };
 
 // most pieces per row of the last round (kSparseTail)
@@ -109,6 +113,9 @@ struct AttnArgs {
   // pair_len[h Bp + I] entries; Bp = ceil(B / 2)
   const int32_t* pair_cols;
   const int32_t* pair_len;
+  // kSparseFused / kSparseTail at b = 128: optional order of each head's
+  // query blocks (row_perm[h B + p] = the block worked p-th); null: identity
+  const int32_t* row_perm;
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
@@ -182,10 +189,11 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
         nt_csr = max(0, min(a.pair_len[item], bp));
       } else {
         h = item / d.B;
-        qp0 = (item - h * d.B) * QT;
-        const int r0 = a.row_ptr[item];
+        const int row = a.row_perm ? h * d.B + a.row_perm[item] : item;
+        qp0 = (row - h * d.B) * QT;
+        const int r0 = a.row_ptr[row];
         cols = a.col_idx + r0;
-        nt_csr = max(0, min(a.row_ptr[item + 1] - r0, d.B));  // a valid row never exceeds B
+        nt_csr = max(0, min(a.row_ptr[row + 1] - r0, d.B));  // a valid row never exceeds B
       }
       nt = nt_csr * TPB + (a.patch_only ? 0 : d.ns_pad / KT);
     } else if constexpr (MODE == kDense) {
@@ -678,6 +686,43 @@ static hipError_t launch_pair_csr(const Dims& d, const int32_t* row_ptr, const i
   return hipGetLastError();
 }
 
+// Order of each head's query blocks for the patch rows: longest kept list
+// first, ties by block index (a bitonic sort of (B - length, block) keys in
+// LDS, one workgroup per head; B <= 4096).
+__global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ row_ptr,
+                                                         Dims d, int32_t* __restrict__ perm) {
+  __shared__ uint32_t key[4096];
+  const int h = wg_x(), T = lid_x();
+  int n2 = 1;
+  while (n2 < d.B) n2 <<= 1;
+  for (int i = T; i < n2; i += 1024) {
+    uint32_t k = 0xffffffffu;
+    if (i < d.B) {
+      const int r = h * d.B + i;
+      const int len = max(0, min(row_ptr[r + 1] - row_ptr[r], d.B));
+      k = ((uint32_t)(d.B - len) << 13) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = T; i < n2; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint32_t x = key[i], y = key[j];
+          if ((x > y) == up) {
+            key[i] = y;
+            key[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = T; i < d.B; i += 1024) perm[h * d.B + i] = (int32_t)(key[i] & 0x1fffu);
+}
+
 // Rows that kSparseTail split into pieces: workgroup (XCD x and tail row
 // t < tmax, the largest leftover of any XCD; group g of 4 query rows) merges
 // the row's float32 partials by
@@ -689,7 +734,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          uint16_t* __restrict__ o,
                                                          float* __restrict__ lse, Dims d,
                                                          int rows, int rows_per_xcd, int m,
-                                                         int pieces, int tmax, int rows_per_head) {
+                                                         int pieces, int tmax, int rows_per_head,
+                                                         const int32_t* __restrict__ row_perm) {
   constexpr int QT = 128;
   const int x = wg_x() / tmax, t = wg_x() % tmax;
   const int r0 = x * rows_per_xcd;
@@ -721,7 +767,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
     l += li[pc] * wgt;
   }
   const int h = item / rows_per_head;
-  const int tok = packed_token((item - h * rows_per_head) * QT + qr, d);
+  const int blk = row_perm ? row_perm[item] : item - h * rows_per_head;
+  const int tok = packed_token(blk * QT + qr, d);
   if (tok < 0) return;
   o[((size_t)h * d.n + tok) * kHeadDim + dim] =
       __builtin_bit_cast(uint16_t, (__bf16)(l > 0.f ? acc / l : 0.f));
@@ -970,8 +1017,11 @@ static size_t tail_part_o_bytes(const TailPlan& p) {
 static size_t tail_bytes(const TailPlan& p) {
   return tail_part_o_bytes(p) + (size_t)p.slots * 128 * 2 * sizeof(float);
 }
+static size_t perm_bytes(const Dims& d) {
+  return d.B <= 4096 ? (((size_t)d.H * d.B * sizeof(int32_t) + 255) & ~(size_t)255) : 0;
+}
 size_t patch_rows_workspace(const Dims& d) {
-  if (d.b == 128) return tail_bytes(tail_plan(d, d.B));
+  if (d.b == 128) return tail_bytes(tail_plan(d, d.B)) + perm_bytes(d);
   if (!pairable(d)) return 0;  // the unpaired 64-row kernel needs none
   return pair_cols_bytes(d) + pair_len_bytes(d) + tail_bytes(tail_plan(d, pair_rows(d)));
 }
@@ -981,6 +1031,14 @@ static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, 
                                   size_t tail_ws_bytes, hipStream_t st) {
   a.n_items = d.H * rows_per_head;
   const TailPlan p = tail_plan(d, rows_per_head);
+  if (!PAIR && tail_ws != nullptr && perm_bytes(d) > 0 &&
+      tail_ws_bytes >= tail_bytes(p) + perm_bytes(d)) {
+    int32_t* perm = (int32_t*)((char*)tail_ws + tail_bytes(p));
+    row_order_kernel<<<d.H, 1024, 0, st>>>(a.row_ptr, d, perm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.row_perm = perm;
+  }
   if (tail_ws != nullptr && p.slots > 0 && tail_ws_bytes >= tail_bytes(p)) {
     a.part_o = (float*)tail_ws;
     a.part_ml = (float*)((char*)tail_ws + tail_part_o_bytes(p));
@@ -992,7 +1050,7 @@ static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, 
     if (e != hipSuccess) return e;
     tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
         a.part_o, a.part_ml, a.o, a.lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem,
-        rows_per_head);
+        rows_per_head, a.row_perm);
     return hipGetLastError();
   }
   attn_kernel<128, 128, kSparseFused, 3, PAIR><<<xcd_grid(a.n_items), 256, 0, st>>>(a);

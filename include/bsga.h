@@ -328,8 +328,7 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     writes its final row of o/lse (equal to bsga_sparse_attn followed by the
  *     merge in bsga_special_dense, without the intermediate bf16 rounding).
  *     Optional workspace (NULL, or bsga_workspace_bytes(
- *     BSGA_OP_PATCH_ROWS_PACKED) bytes; at b = 128 it is 0 when splitting
- *     would not shorten the last round; at b = 64 it is 0 when B > 8192).
+ *     BSGA_OP_PATCH_ROWS_PACKED) bytes; at b = 64 it is 0 when B > 8192).
  *     At b = 64 (B <= 8192) a workspace lets the call run query blocks in
  *     aligned pairs: query blocks 2I, 2I + 1 form a
  *     128-query tile that walks the 128-key tiles (key blocks 2J, 2J + 1)
@@ -343,7 +342,12 @@ int bsga_dense_attn_packed(const bsga_shape* shape, const uint16_t* q,
  *     count, at most 16, whose pieces finish first, if that is under 0.8 of
  *     a block's time) whose float32 partials are merged by log-sum-exp
  *     afterwards, which balances that round; the result is the same softmax
- *     (it may differ from the unsplit rows in the last bit).  The plan uses
+ *     (it may differ from the unsplit rows in the last bit).  At b = 128
+ *     with B <= 4096 the workspace also holds an order of each head's query
+ *     blocks, longest kept list first (ties by block index), which the
+ *     workgroups follow: concurrent workgroups then hold rows of similar
+ *     length and the split last round the shortest rows (every row's result
+ *     is the same as in natural order, the split rows aside).  The plan uses
  *     the compute-unit count of the current device: size and use the
  *     workspace with the same device current;
  *   bsga_special_rows_packed: every special query attends to all N tokens

@@ -98,19 +98,20 @@ def test_capacity_and_workspace_sizes():
     out = ctypes.c_size_t()
     assert bsga.workspace_bytes(shape, bsga.OP_BACKWARD) >= 7 * 16 * 44032 * 128
     # patch rows at b = 128: float32 partials (64 values, max and sum per
-    # query) of the last round's split rows.  Without a device the plan
+    # query) of the last round's split rows, then the order of the query
+    # blocks (one int32 per row, for B <= 4096).  Without a device the plan
     # assumes 96 workgroup slots per XCD: 5488 rows are 686 per XCD, 14 of
     # them in the last round, split into 96 // 14 = 6 pieces each
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
     tail = bsga.workspace_bytes(shape, bsga.OP_PATCH_ROWS_PACKED)
     assert tail_bytes(5488, 343) == 8 * 14 * 6 * 128 * 66 * 4
-    assert tail_bytes(5488, 343) <= tail <= tail_bytes(5488, 343) + 512
+    assert tail_bytes(5488, 343) + up(5488 * 4) <= tail <= tail_bytes(5488, 343) + up(5488 * 4) + 512
     assert bsga.workspace_bytes(shape, bsga.OP_LAYER) >= tail
     # patch rows at b = 64: the aligned-pair lists (a key-tile list of up to
     # ceil(B / 2) entries and its length per pair of query blocks), then the
     # split last round of the pair rows.  The 8-frame layer: B = 172, 86 pair
     # rows per head, 1376 rows, 172 per XCD, 76 in the last round of 96
     # slots: no piece count shortens it
-    up = lambda x: -(-x // 256) * 256  # noqa: E731
     pairs = up(16 * 86 * 86 * 4) + up(16 * 86 * 4)
     assert tail_bytes(1376, 86) == 0
     assert bsga.workspace_bytes(S(8, 1369, 5, 16, 64), bsga.OP_PATCH_ROWS_PACKED) == pairs
@@ -128,21 +129,24 @@ def test_capacity_and_workspace_sizes():
     # 400 rows (16 heads x 25 blocks): 50 per XCD, more than half a round: 3
     # pieces each, in two rounds of a third of a row
     assert tail_pieces(50, 25) == 3 and tail_bytes(400, 25) == 8 * 50 * 3 * 128 * 66 * 4
-    assert tail_bytes(400, 25) <= bsga.workspace_bytes(S(1, 3200, 5, 16, 128),
-                                                   bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(400, 25) + 512
+    assert tail_bytes(400, 25) + up(400 * 4) <= bsga.workspace_bytes(
+        S(1, 3200, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(400, 25) + up(400 * 4) + 512
     # the 100- and 200-frame layers: 64 and 56 of 96 slots in the last round
     assert tail_pieces(64, 608) == 3 and tail_pieces(56, 2140) == 12
     # 720 rows (16 x 45): 90 per XCD, no piece count shortens the round
     assert tail_pieces(90, 45) == 0
-    assert bsga.workspace_bytes(S(1, 5760, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) <= 1
+    assert bsga.workspace_bytes(S(1, 5760, 5, 16, 128), bsga.OP_PATCH_ROWS_PACKED) == up(720 * 4)
+    # past B = 4096 the rows keep their natural order: no order array
+    assert tail_bytes(4097, 4097) <= bsga.workspace_bytes(
+        S(1, 4097 * 128, 0, 1, 128), bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(4097, 4097) + 512
     # 8 rows: one per XCD, split into the most pieces (16)
     assert tail_bytes(8, 8) == 8 * 1 * 16 * 128 * 66 * 4
-    assert tail_bytes(8, 8) <= bsga.workspace_bytes(S(1, 1024, 5, 1, 128),
-                                                 bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(8, 8) + 512
+    assert tail_bytes(8, 8) + up(8 * 4) <= bsga.workspace_bytes(
+        S(1, 1024, 5, 1, 128), bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(8, 8) + up(8 * 4) + 512
     # 64 rows: 8 per XCD, 96 // 8 = 12 pieces
     assert tail_bytes(64, 8) == 8 * 8 * 12 * 128 * 66 * 4
-    assert tail_bytes(64, 8) <= bsga.workspace_bytes(S(1, 1024, 5, 8, 128),
-                                                  bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(64, 8) + 512
+    assert tail_bytes(64, 8) + up(64 * 4) <= bsga.workspace_bytes(
+        S(1, 1024, 5, 8, 128), bsga.OP_PATCH_ROWS_PACKED) <= tail_bytes(64, 8) + up(64 * 4) + 512
     assert lib.bsga_workspace_bytes(ctypes.byref(shape.c()), bsga.OP_PATCH_ROWS_PACKED + 1,
                                     ctypes.byref(out)) == bsga.ERR_INVALID_ARG
 

@@ -448,11 +448,24 @@ def test_end_to_end_mask_vs_oracle_pipeline(lib):
             f"(nnz gpu {rp[-1]}, oracle {orp[-1]})")
 
 
-def _split_rows(rows, blocks, m, xcds=8):
+def _row_order(row_ptr, heads, blocks):
+    """The order the patch-row call (with a workspace, B <= 4096) works each
+    head's query blocks in: longest kept list first, ties by block index.
+    Returns, per head-major position, the head-major row."""
+    lens = np.diff(np.asarray(row_ptr, dtype=np.int64)).clip(0, blocks).reshape(heads, blocks)
+    out = []
+    for h in range(heads):
+        order = sorted(range(blocks), key=lambda i: (-int(lens[h, i]), i))
+        out += [h * blocks + i for i in order]
+    return out
+
+
+def _split_rows(rows, blocks, m, xcds=8, order=None):
     """Rows (head-major query blocks) that the patch-row call at b = 128 runs
-    as key-range pieces: those of each XCD's last, partial round of m
-    workgroup slots (rows are dealt to XCDs in equal contiguous ranges),
-    unless no piece count shortens that round."""
+    as key-range pieces: those at the positions of each XCD's last, partial
+    round of m workgroup slots (positions are dealt to XCDs in equal
+    contiguous ranges; ``order`` maps a position to its row), unless no piece
+    count shortens that round."""
     from test_abi_host import tail_pieces
     per = -(-rows // xcds)
     rems = [(min(rows, (x + 1) * per) - x * per) % m for x in range(xcds)
@@ -467,15 +480,17 @@ def _split_rows(rows, blocks, m, xcds=8):
             break
         full = n_x // m * m
         out += list(range(r0 + full, r0 + n_x))
-    return out
+    return [order[p] for p in out] if order is not None else out
 
 
 @pytest.mark.parametrize("name", ["vggt-32f", "ragged-b128", "over-half-b128"])
 def test_patch_rows_tail_pieces(lib, name):
-    """bsga_patch_rows_packed with its workspace splits the rows of the last,
-    partial round into key-range pieces and merges them: those rows (every
-    query) match the oracle within the usual bars, and every other row is
-    byte-identical to the call without workspace (one workgroup per row)."""
+    """bsga_patch_rows_packed with its workspace works each head's query
+    blocks longest kept list first and splits the rows of the last, partial
+    round (the shortest) into key-range pieces, merged afterwards: those rows
+    (every query) match the oracle within the usual bars, and every other row
+    is byte-identical to the call without workspace (one workgroup per row,
+    natural order)."""
     import torch
     from gpu_helpers import compare_rows, from_dev_bf16, layer_shape, oracle_rows, say
     x = inputs(name)
@@ -493,7 +508,8 @@ def test_patch_rows_tail_pieces(lib, name):
     torch.cuda.synchronize()
     B = lib.num_blocks(shape)
     m = 3 * torch.cuda.get_device_properties(0).multi_processor_count // 8
-    split = _split_rows(cfg.heads * B, B, m)
+    split = _split_rows(cfg.heads * B, B, m,
+                        order=_row_order(row_ptr.cpu().numpy(), cfg.heads, B))
     say(f"[tail pieces] {name}: {len(split)} of {cfg.heads * B} query blocks split, {m} slots/XCD")
     assert split, "the shape should leave a partial last round"
     rp = row_ptr.cpu().numpy().astype(np.int64)
@@ -529,8 +545,9 @@ def test_patch_rows_tail_pieces(lib, name):
 def test_patch_rows_unsplit_when_last_round_large(lib):
     """720 query blocks (16 heads x 45) leave 90 per XCD for the last round of
     96 slots: no piece count shortens it, so the plan splits nothing, the
-    workspace is empty, and the call with a workspace is byte-identical to
-    the one without."""
+    workspace holds only the order of the query blocks (one int32 per row),
+    and the call with a workspace (longest rows first) is byte-identical to
+    the one without (natural order)."""
     import torch
     from gpu_helpers import layer_shape, say
     x = synth.random_layer(1, 72, 80, 16, 128, seed=21)
@@ -540,7 +557,7 @@ def test_patch_rows_unsplit_when_last_round_large(lib):
     m = 3 * torch.cuda.get_device_properties(0).multi_processor_count // 8
     if _split_rows(cfg.heads * B, B, m):
         pytest.skip(f"{m} slots per XCD split this shape")
-    assert lib.workspace_bytes(shape, lib.OP_PATCH_ROWS_PACKED) <= 1
+    assert lib.workspace_bytes(shape, lib.OP_PATCH_ROWS_PACKED) == -(-cfg.heads * B * 4 // 256) * 256
     q, k, v = _upload(x)
     probs = lib.predict_mask(shape, q, k)
     row_ptr, col_idx = lib.select(shape, probs, cfg.rho, cfg.tau)
