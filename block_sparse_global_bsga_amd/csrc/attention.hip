@@ -687,16 +687,18 @@ static hipError_t launch_pair_csr(const Dims& d, const int32_t* row_ptr, const i
 }
 
 // Order of each head's query blocks for the patch rows: longest kept list
-// first, ties by block index (a bitonic sort of (B - length, block) keys in
-// LDS, one workgroup per head; B <= 4096).
-__global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ row_ptr,
-                                                         Dims d, int32_t* __restrict__ perm) {
-  __shared__ uint32_t key[4096];
-  const int h = wg_x(), T = lid_x();
-  int n2 = 1;
-  while (n2 < d.B) n2 <<= 1;
-  for (int i = T; i < n2; i += 1024) {
-    uint32_t k = 0xffffffffu;
+// first, ties by block index.  Each block's key (B - length, block) is
+// unique, so its position in the order is its rank, the number of smaller
+// keys: workgroup (x, h) holds the B keys of head h in LDS and ranks blocks
+// 256 x .. 256 x + 255 against all of them (B <= 4096).
+__global__ __launch_bounds__(256) void row_order_kernel(const int32_t* __restrict__ row_ptr,
+                                                        Dims d, int32_t* __restrict__ perm) {
+  __shared__ uint4 key4[1024];
+  uint32_t* key = (uint32_t*)key4;
+  const int h = wg_y(), T = lid_x();
+  const int nb4 = (d.B + 3) >> 2;
+  for (int i = T; i < 4 * nb4; i += 256) {
+    uint32_t k = 0xffffffffu;  // padding: above every real key
     if (i < d.B) {
       const int r = h * d.B + i;
       const int len = max(0, min(row_ptr[r + 1] - row_ptr[r], d.B));
@@ -705,22 +707,15 @@ __global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restri
     key[i] = k;
   }
   __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = T; i < n2; i += 1024) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const uint32_t x = key[i], y = key[j];
-          if ((x > y) == up) {
-            key[i] = y;
-            key[j] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  for (int i = T; i < d.B; i += 1024) perm[h * d.B + i] = (int32_t)(key[i] & 0x1fffu);
+  const int i = wg_x() * 256 + T;
+  if (i >= d.B) return;
+  const uint32_t k = key[i];
+  int rank = 0;
+  for (int j = 0; j < nb4; ++j) {
+    const uint4 q = key4[j];
+    rank += (q.x < k) + (q.y < k) + (q.z < k) + (q.w < k);
+  }
+  perm[h * d.B + rank] = i;
 }
 
 // Rows that kSparseTail split into pieces: workgroup (XCD x and tail row
@@ -1034,7 +1029,7 @@ static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, 
   if (!PAIR && tail_ws != nullptr && perm_bytes(d) > 0 &&
       tail_ws_bytes >= tail_bytes(p) + perm_bytes(d)) {
     int32_t* perm = (int32_t*)((char*)tail_ws + tail_bytes(p));
-    row_order_kernel<<<d.H, 1024, 0, st>>>(a.row_ptr, d, perm);
+    row_order_kernel<<<dim3((d.B + 255) / 256, d.H), 256, 0, st>>>(a.row_ptr, d, perm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.row_perm = perm;

@@ -401,9 +401,10 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
   // compile-time constant.
   f32x16 g0 = {}, g1 = {};  // dQ^T: dims 0-31 and 32-63 x the wave's 32 queries
   float d_lane = 0.f, dq_d = 0.f;
-  for (int sweep = 0; sweep < 2; ++sweep) {
-    const bool second = sweep == 1;
-    if (nt == 0) break;
+  // each sweep is its own instance of the tile loop (its registers and
+  // branches specialised to what it computes)
+  auto sweep = [&](auto second_tag) {
+    constexpr bool second = decltype(second_tag)::value;
     int raw_cur = tile_raw(0), raw_nxt = tile_raw(1);
     issue(tile_kp0(0, raw_cur), 0, second);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -429,14 +430,13 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_op(smem, vb + op.row[m] + t * kSubRows),
                                                          dop[m], dp, 0, 0, 0);
           }
-          if (!second) {
+          if constexpr (!second) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float p = fast_exp2(fmaf(s[r], kScaleLog2, -lse2));
               d_lane = fmaf((kFull || 32 * t + acc_row(r) < lim) ? p : 0.f, dp[r], d_lane);
             }
-            continue;
-          }
+          } else {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             f32x8 e8, rem;
@@ -457,6 +457,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
             g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
             g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_lo, g1, 0, 0, 0);
           }
+          }
         }
       };
       if (valid == KT) tile(std::true_type{});
@@ -472,10 +473,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
       step(std::integral_constant<int, 1>{}, n);
       if (++n == nt) break;
     }
-    if (!second) {
+    if constexpr (!second) {
       dq_d = xor32_sum(d_lane);  // lanes l and l + 32 hold the same query
       if (hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = dq_d;
     }
+  };
+  if (nt > 0) {
+    sweep(std::false_type{});
+    sweep(std::true_type{});
   }
   if (nt == 0 && hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = 0.f;
   const int tok = packed_token(qrow, d);
