@@ -10,7 +10,8 @@
 // CSR row (sparse), every tile (dense), a range of tiles (split-K for the
 // special queries) or the special-token tiles (patch queries x special keys).
 //
-// Data flow per key tile, per wave (v_mfma_f32_32x32x16_bf16 throughout):
+// Data flow per key tile, per wave (32x32x16 MFMAs: bf16 for the scores,
+// float16 for P V):
 //   S^T (keys x queries) = K Q^T : K rows from LDS are the A operand, the
 //     wave's 32 query rows stay in registers as the B operand.  Lane l then
 //     holds the 16 scores of query l%32 for one half of each 32-key sub-tile.

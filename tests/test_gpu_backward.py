@@ -7,8 +7,9 @@ in float64 on the same bf16 inputs.  Bar, per gradient tensor of a head:
 max |g_gpu - g_oracle| <= 2e-2 * rms(g_oracle).  (With P and dS as single
 bf16 operands and D from the stored bf16 O, dQ missed this by an order of
 magnitude on the peaked synthetic heads, since a query's dS are small
-differences that sum to zero; the kernels therefore use hi + lo operands and
-recompute D from P and dP.)
+differences that sum to zero; the kernels therefore feed dS to the dQ and dK
+products as a bf16 pair hi + lo, P to the dV product once as float16 (11
+significant bits), and recompute D from P and dP.)
 """
 from __future__ import annotations
 

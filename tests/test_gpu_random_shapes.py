@@ -25,8 +25,8 @@ Per shape, through the C ABI:
   softmax rows are one-hot to float64 precision (a planted correspondence
   with itself as the only match) has dQ and dK near 1e-30, and float32
   rounding of dS = P (dP - D), far below the terms' size, would count as
-  error; the floor is still 2^-15 of that size, above the hi + lo
-  arithmetic's rounding.
+  error; the floor is still 2^-15 of that size, above the rounding of dS
+  (a bf16 pair hi + lo) in the dQ and dK products.
 """
 from __future__ import annotations
 
