@@ -409,7 +409,20 @@ def main():
         bwd_tflops = BWD_FLOP_PER_ENTRY * (ppb + spb) / (bwd_ms * 1e-3) / 1e12
         print(f"# backward {bwd_ms:.3f} ms ({bwd_tflops:.0f} TFLOP/s)", file=sys.stderr,
               flush=True)
-        del grads, ws_bwd, d_o
+        # training mode: the forward writes float32 rows (P V with P as a
+        # float16 pair hi + lo), and the backward takes D = dO . O from them
+        bufs_t = bsga.LayerBuffers(shape, dev)
+        o32 = torch.empty((cfg.heads, n, HEAD_DIM), dtype=torch.float32, device=dev)
+        train_ms, _ = timed(lambda _ev: bsga.layer_train(shape, q, k, v, cfg.rho, cfg.tau,
+                                                         x.rho_per_head, bufs=bufs_t, o32=o32),
+                            max(3, args.steps // 2), 2)
+        bwd32_ms, _ = timed(lambda _ev: bsga.attn_backward(
+            shape, q, k, v, o32, bufs_t.lse, d_o, bufs_t.row_ptr, bufs_t.col_idx,
+            dq=grads[0], dk=grads[1], dv=grads[2], ws=ws_bwd), max(3, args.steps // 2), 2)
+        bwd32_tflops = BWD_FLOP_PER_ENTRY * (ppb + spb) / (bwd32_ms * 1e-3) / 1e12
+        print(f"# training: layer {train_ms:.3f} ms + backward from o32 {bwd32_ms:.3f} ms",
+              file=sys.stderr, flush=True)
+        del grads, ws_bwd, d_o, bufs_t, o32
         extras = {
             "probe_topk": {"topk": topk, "select_ms": round(probe_parts[0], 4),
                            "select_GB/s": round(probe_bytes / (probe_parts[0] * 1e-3) / 1e9, 1),
@@ -422,6 +435,15 @@ def main():
                          "flop_per_entry": BWD_FLOP_PER_ENTRY,
                          "TFLOP/s": round(bwd_tflops, 1),
                          "frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4)},
+            "training": {"note": "bsga_layer_train (float32 rows, P V with P as an fp16 "
+                                 "pair hi + lo) then bsga_attn_backward_o32 (D = dO . O from "
+                                 "them); compare bsga_layer + bsga_attn_backward",
+                         "layer_train_ms": round(train_ms, 4),
+                         "backward_o32_ms": round(bwd32_ms, 4),
+                         "backward_o32_TFLOP/s": round(bwd32_tflops, 1),
+                         "backward_o32_frac_peak": round(bwd32_tflops / PEAK_BF16_TFLOPS, 4),
+                         "forward_plus_backward_ms": round(train_ms + bwd32_ms, 4),
+                         "inference_forward_plus_backward_ms": round(layer_call_ms + bwd_ms, 4)},
             "step_latency_median_ms": {"warm": round(warm_median, 4),
                                        "flushed_512MB": round(flushed_median, 4),
                                        "steps": lat_reps},

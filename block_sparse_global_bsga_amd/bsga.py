@@ -40,7 +40,7 @@ EXPORTS = [
     "bsga_layer", "bsga_packed_kv_bytes", "bsga_pack_kv", "bsga_sparse_attn_packed",
     "bsga_special_dense_packed", "bsga_dense_attn_packed", "bsga_patch_rows_packed",
     "bsga_special_rows_packed", "bsga_redistribute", "bsga_probe_select", "bsga_nmse",
-    "bsga_attn_backward", "bsga_select_static",
+    "bsga_attn_backward", "bsga_select_static", "bsga_layer_train", "bsga_attn_backward_o32",
 ]
 
 
@@ -86,6 +86,10 @@ _lib.bsga_special_rows_packed.argtypes = [_sp, _p, _p, ctypes.c_size_t, _p, _p, 
                                           ctypes.c_size_t, _p]
 _lib.bsga_layer.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p, _p,
                             ctypes.c_int64, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.bsga_layer_train.argtypes = [_sp, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double, _p, _p,
+                                  _p, ctypes.c_int64, _p, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.bsga_attn_backward_o32.argtypes = [_sp, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                        ctypes.c_size_t, _p]
 
 
 class BsgaError(RuntimeError):
@@ -314,9 +318,14 @@ def nmse(shape: LayerShape, o_ref: torch.Tensor, o: torch.Tensor, *,
 def attn_backward(shape: LayerShape, q, k, v, o, lse, d_o, row_ptr, col_idx, *,
                   dq=None, dk=None, dv=None, ws: Optional[torch.Tensor] = None):
     """Gradients (dQ, dK, dV) [H][N][64] float32 of the layer's attention for
-    the mask (row_ptr, col_idx) that produced o and lse."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+    the mask (row_ptr, col_idx) that produced o and lse.  o: the bf16 rows
+    (bsga_attn_backward), or the float32 rows of layer_train
+    (bsga_attn_backward_o32)."""
+    o32 = o.dtype == torch.float32
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")) + (() if o32 else ((o, "o"),)):
         _bf16(t, n, shape)
+    if o32 and (tuple(o.shape) != (shape.heads, shape.tokens, 64) or not o.is_contiguous()):
+        raise ValueError("o (float32) must be a contiguous [H][N][64] tensor")
     dev = q.device
     grads = []
     for g in (dq, dk, dv):
@@ -325,10 +334,11 @@ def attn_backward(shape: LayerShape, q, k, v, o, lse, d_o, row_ptr, col_idx, *,
         grads.append(g)
     if ws is None:
         ws = workspace(shape, OP_BACKWARD, dev)
-    _check(_lib.bsga_attn_backward(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                   _ptr(lse), _ptr(d_o), _ptr(row_ptr), _ptr(col_idx),
-                                   *[_ptr(g) for g in grads], _ws_ptr(ws), _ws_len(ws),
-                                   _stream(dev)), "bsga_attn_backward")
+    fn, name = ((_lib.bsga_attn_backward_o32, "bsga_attn_backward_o32") if o32 else
+                (_lib.bsga_attn_backward, "bsga_attn_backward"))
+    _check(fn(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+              _ptr(row_ptr), _ptr(col_idx), *[_ptr(g) for g in grads], _ws_ptr(ws), _ws_len(ws),
+              _stream(dev)), name)
     return tuple(grads)
 
 
@@ -479,3 +489,24 @@ def layer(shape: LayerShape, q, k, v, rho: float, tau: float,
                            _ws_len(bufs.ws), _stream(q.device)), "bsga_layer")
     del keep
     return bufs
+
+
+def layer_train(shape: LayerShape, q, k, v, rho: float, tau: float,
+                rho_per_head: Optional[Sequence[float]] = None, *,
+                bufs: Optional[LayerBuffers] = None, o32: Optional[torch.Tensor] = None):
+    """bsga_layer_train: the layer with P as a float16 pair hi + lo in the P V
+    products and the final rows also as float32.  Returns (bufs, o32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16(t, n, shape)
+    if bufs is None:
+        bufs = LayerBuffers(shape, q.device)
+    if o32 is None:
+        o32 = torch.empty((shape.heads, shape.tokens, 64), dtype=torch.float32, device=q.device)
+    keep, rp = _rho_array(shape, rho_per_head)
+    _check(_lib.bsga_layer_train(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), rp,
+                                 float(rho), float(tau), _ptr(bufs.probs), _ptr(bufs.row_ptr),
+                                 _ptr(bufs.col_idx), bufs.col_idx.numel(), _ptr(bufs.o),
+                                 _ptr(bufs.lse), _ptr(o32), _ws_ptr(bufs.ws), _ws_len(bufs.ws),
+                                 _stream(q.device)), "bsga_layer_train")
+    del keep
+    return bufs, o32

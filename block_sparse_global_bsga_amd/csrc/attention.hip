@@ -117,6 +117,9 @@ struct AttnArgs {
   // kSparseFused / kSparseTail at b = 128: optional order of each head's
   // query blocks (row_perm[h B + p] = the block worked p-th); null: identity
   const int32_t* row_perm;
+  // attn_kernel<..., O32 = true>: [H][N][64] float32 copy of the final rows
+  // (the value O holds before its bf16 rounding), for the backward
+  float* o32;
 };
 
 // A tile is exponentiated against a stale running max as long as its exact
@@ -132,7 +135,11 @@ constexpr int kBufWord3 = 0x00020000;
 // QT query rows per workgroup (QT / 32 waves), KT keys per tile, WPE waves
 // per SIMD targeted (bounds the registers of a wave to 512 / WPE).
 // PAIR: b = 64 blocks run as aligned pairs (AttnArgs::pair) on QT = KT = 128
-template <int QT, int KT, int MODE, int WPE, bool PAIR = false>
+// O32: training mode: P enters the P V product as a float16 pair hi + lo
+// (about 22 significant bits, against 11 for hi alone) and the final rows are
+// also written as float32 to AttnArgs::o32, so that the backward can take
+// D = dO . O from them
+template <int QT, int KT, int MODE, int WPE, bool PAIR = false, bool O32 = false>
 __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_kernel(
     AttnArgs a) {
   constexpr int NW = QT / 32;       // waves
@@ -477,6 +484,14 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
           const f16x8 pb = __builtin_convertvector(e8, f16x8);
           o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[h2], pb, o0, 0, 0, 0);
           o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[h2], pb, o1, 0, 0, 0);
+          if constexpr (O32) {
+            f32x8 rem;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)pb[e];
+            const f16x8 pl = __builtin_convertvector(rem, f16x8);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[h2], pl, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[h2], pl, o1, 0, 0, 0);
+          }
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -544,6 +559,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(WPE, WPE
           x[3] += cp * __uint_as_float(old[1] & 0xffff0000u);
         }
         *dst = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+        if constexpr (O32)
+          *(f32x4*)(a.o32 + ((size_t)h * d.n + qtok) * kHeadDim + 32 * u + 8 * aa + 4 * hh) = x;
       }
     };
     store_half(o0, 0);
@@ -582,7 +599,7 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
                                                              const float* __restrict__ part_ml,
                                                              uint16_t* __restrict__ o,
                                                              float* __restrict__ lse, Dims d,
-                                                             int nsplit) {
+                                                             int nsplit, float* __restrict__ o32) {
   const int item = wg_x() * 4 + (lid_x() >> 6);
   const int lane = lid_x() & 63;
   if (item >= d.H * d.ns) return;
@@ -617,8 +634,9 @@ __global__ __launch_bounds__(256) void special_reduce_kernel(const float* __rest
     }
   }
   const int tok = special_token(s, d);
-  o[((size_t)h * d.n + tok) * kHeadDim + lane] =
-      __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
+  const float val = acc / L;
+  o[((size_t)h * d.n + tok) * kHeadDim + lane] = __builtin_bit_cast(uint16_t, (__bf16)val);
+  if (o32 != nullptr) o32[((size_t)h * d.n + tok) * kHeadDim + lane] = val;
   if (lane == 0) lse[(size_t)h * d.n + tok] = M * 0.125f + logf(L);
 }
 
@@ -731,7 +749,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
                                                          float* __restrict__ lse, Dims d,
                                                          int rows, int rows_per_xcd, int m,
                                                          int pieces, int tmax, int rows_per_head,
-                                                         const int32_t* __restrict__ row_perm) {
+                                                         const int32_t* __restrict__ row_perm,
+                                                         float* __restrict__ o32) {
   constexpr int QT = 128;
   const int x = wg_x() / tmax, t = wg_x() % tmax;
   const int r0 = x * rows_per_xcd;
@@ -766,8 +785,9 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(const float* __restrict
   const int blk = row_perm ? row_perm[item] : item - h * rows_per_head;
   const int tok = packed_token(blk * QT + qr, d);
   if (tok < 0) return;
-  o[((size_t)h * d.n + tok) * kHeadDim + dim] =
-      __builtin_bit_cast(uint16_t, (__bf16)(l > 0.f ? acc / l : 0.f));
+  const float val = l > 0.f ? acc / l : 0.f;
+  o[((size_t)h * d.n + tok) * kHeadDim + dim] = __builtin_bit_cast(uint16_t, (__bf16)val);
+  if (o32 != nullptr) o32[((size_t)h * d.n + tok) * kHeadDim + dim] = val;
   if (dim == 0)
     lse[(size_t)h * d.n + tok] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
@@ -1022,7 +1042,7 @@ size_t patch_rows_workspace(const Dims& d) {
   return pair_cols_bytes(d) + pair_len_bytes(d) + tail_bytes(tail_plan(d, pair_rows(d)));
 }
 
-template <bool PAIR>
+template <bool PAIR, bool O32 = false>
 static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, void* tail_ws,
                                   size_t tail_ws_bytes, hipStream_t st) {
   a.n_items = d.H * rows_per_head;
@@ -1041,26 +1061,34 @@ static hipError_t launch_rows_128(const Dims& d, AttnArgs a, int rows_per_head, 
     a.rows_per_xcd = p.rows_per_xcd;
     a.tail_m = p.m;
     a.tail_pieces = p.pieces;
-    attn_kernel<128, 128, kSparseTail, 3, PAIR><<<kXcds * p.grid, 256, 0, st>>>(a);
+    attn_kernel<128, 128, kSparseTail, 3, PAIR, O32><<<kXcds * p.grid, 256, 0, st>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     tail_merge_kernel<<<dim3(kXcds * p.max_rem, 128 / 4), 256, 0, st>>>(
         a.part_o, a.part_ml, a.o, a.lse, d, p.rows, p.rows_per_xcd, p.m, p.pieces, p.max_rem,
-        rows_per_head, a.row_perm);
+        rows_per_head, a.row_perm, O32 ? a.o32 : nullptr);
     return hipGetLastError();
   }
-  attn_kernel<128, 128, kSparseFused, 3, PAIR><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+  attn_kernel<128, 128, kSparseFused, 3, PAIR, O32><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
+bool patch_rows_train_supported(const Dims& d) { return d.b == 128 || pairable(d); }
+
+// o32 != null (training mode) needs a workspace and b = 128 or aligned pairs
+// (b = 64, B <= 8192); the caller checks both.
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                              const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                             uint16_t* o, float* lse, hipStream_t st, void* ws, size_t ws_bytes) {
+                             uint16_t* o, float* lse, hipStream_t st, void* ws, size_t ws_bytes,
+                             float* o32) {
   AttnArgs a = base_args(d, q, kp, vt, o, lse);
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.n_items = d.H * d.B;
-  if (ws != nullptr && d.b == 128) return launch_rows_128<false>(d, a, d.B, ws, ws_bytes, st);
+  a.o32 = o32;
+  if (ws != nullptr && d.b == 128)
+    return o32 ? launch_rows_128<false, true>(d, a, d.B, ws, ws_bytes, st)
+               : launch_rows_128<false>(d, a, d.B, ws, ws_bytes, st);
   if (ws != nullptr && pairable(d) && ws_bytes >= pair_cols_bytes(d) + pair_len_bytes(d)) {
     int32_t* pc = (int32_t*)ws;
     int32_t* pl = (int32_t*)((char*)ws + pair_cols_bytes(d));
@@ -1069,8 +1097,11 @@ hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* k
     a.pair_cols = pc;
     a.pair_len = pl;
     const size_t used = pair_cols_bytes(d) + pair_len_bytes(d);
-    return launch_rows_128<true>(d, a, pair_rows(d), (char*)ws + used, ws_bytes - used, st);
+    return o32 ? launch_rows_128<true, true>(d, a, pair_rows(d), (char*)ws + used,
+                                             ws_bytes - used, st)
+               : launch_rows_128<true>(d, a, pair_rows(d), (char*)ws + used, ws_bytes - used, st);
   }
+  if (o32 != nullptr) return hipErrorInvalidValue;
   return run_attn_b<kSparseFused>(d, a, st);
 }
 
@@ -1109,7 +1140,7 @@ size_t special_workspace(const Dims& d) {
 
 hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                                const uint16_t* vt, uint16_t* o, float* lse, void* ws,
-                               hipStream_t st) {
+                               hipStream_t st, float* o32) {
   if (d.ns == 0) return hipSuccess;
   const SplitPlan p = special_plan(d);
   const size_t slots = (size_t)d.H * d.ns_pad * p.nsplit;
@@ -1120,17 +1151,22 @@ hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t*
   a.nsplit = p.nsplit;
   a.tiles_per_split = p.tps;
   a.n_items = d.H * p.q_tiles * p.nsplit;
-  hipError_t e = run_attn<128, 128, kSpecialSplit>(a, st);
+  if (o32 != nullptr)
+    attn_kernel<128, 128, kSpecialSplit, 3, false, true><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+  else
+    attn_kernel<128, 128, kSpecialSplit, 3><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int items = d.H * d.ns;
-  special_reduce_kernel<<<(items + 3) / 4, 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d, p.nsplit);
+  special_reduce_kernel<<<(items + 3) / 4, 256, 0, st>>>(a.part_o, a.part_ml, o, lse, d, p.nsplit,
+                                                         o32);
   return hipGetLastError();
 }
 
 hipError_t launch_special(const Dims& d, const uint16_t* q, const uint16_t* kp,
                           const uint16_t* vt, uint16_t* o, float* lse, void* ws, hipStream_t st) {
   if (d.ns == 0) return hipSuccess;
-  hipError_t e = launch_special_rows(d, q, kp, vt, o, lse, ws, st);
+  hipError_t e = launch_special_rows(d, q, kp, vt, o, lse, ws, st, nullptr);
   if (e != hipSuccess) return e;
   AttnArgs b = base_args(d, q, kp, vt, o, lse);
   b.q_tiles = d.np_pad / 128;

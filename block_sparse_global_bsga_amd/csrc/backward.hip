@@ -110,10 +110,12 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(const uint4* __restrict__
 
 // Per packed row: lse2 = LSE * log2(e) (+inf for padding, so every weight of
 // a padding row is 0), lse2s = lse2 - 15 (the weights 2^15 P of dkdv_kernel)
-// and D = dO . O in float32 (0 for padding).  dq_kernel overwrites D for
-// every row of its query tiles with sum_k P dP; rows no query tile covers
-// are padding and keep 0.
+// and D = dO . O in float32 (0 for padding), from the bf16 rows o or, when
+// given, the float32 rows o32 of the training-mode forward.  Without o32,
+// dq_kernel overwrites D for every row of its query tiles with sum_k P dP;
+// rows no query tile covers are padding and keep 0.
 __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restrict__ o,
+                                                           const float4* __restrict__ o32,
                                                            const uint4* __restrict__ d_o,
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ lse2,
@@ -125,12 +127,25 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(const uint4* __restri
   float s = 0.f;
   if (tok >= 0) {
     const size_t at = ((size_t)h * d.n + tok) * 8 + ch;
-    const uint4 a = o[at], b = d_o[at];
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    const uint4 b = d_o[at];
+    const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+    if (o32 != nullptr) {
+      // dims 8 ch .. 8 ch + 7 of the row as two float4
+      const float4 x0 = o32[at * 2], x1 = o32[at * 2 + 1];
+      const float xo[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(wb[e] << 16), s);
-      s = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(wb[e] & 0xffff0000u), s);
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(xo[2 * e], __uint_as_float(wb[e] << 16), s);
+        s = fmaf(xo[2 * e + 1], __uint_as_float(wb[e] & 0xffff0000u), s);
+      }
+    } else {
+      const uint4 a = o[at];
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(wb[e] << 16), s);
+        s = fmaf(__uint_as_float(wa[e] & 0xffff0000u), __uint_as_float(wb[e] & 0xffff0000u), s);
+      }
     }
   }
   s += __shfl_xor(s, 1);
@@ -304,6 +319,7 @@ struct BwdArgs {
   const int* dosig;     // [H] sigma of the float16 dO^T copy
   const float* dd;      // [H][Ntot] D per packed row, read by dkdv_kernel
   float* dd_out;        // the same array, written by dq_kernel
+  int d_given;          // D came from the float32 rows: dq_kernel skips its first sweep
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const int32_t* t_ptr;
@@ -479,10 +495,13 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
     }
   };
   if (nt > 0) {
-    sweep(std::false_type{});
+    if (a.d_given)
+      dq_d = a.dd[(size_t)h * d.ntot_pad + qrow];
+    else
+      sweep(std::false_type{});
     sweep(std::true_type{});
   }
-  if (nt == 0 && hh == 0) a.dd_out[(size_t)h * d.ntot_pad + qrow] = 0.f;
+  if (nt == 0 && hh == 0 && !a.d_given) a.dd_out[(size_t)h * d.ntot_pad + qrow] = 0.f;
   const int tok = packed_token(qrow, d);
   if (tok < 0) return;
   float* out = a.dq + ((size_t)h * d.n + tok) * kHeadDim;
@@ -682,9 +701,9 @@ size_t backward_workspace(const Dims& d) {
 hipError_t launch_scan_counts(const int32_t* counts, int rows, int32_t* row_ptr, hipStream_t st);
 
 hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                           const uint16_t* o, const float* lse, const uint16_t* d_o,
-                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
-                           float* dv, void* ws, hipStream_t st) {
+                           const uint16_t* o, const float* o32, const float* lse,
+                           const uint16_t* d_o, const int32_t* row_ptr, const int32_t* col_idx,
+                           float* dq, float* dk, float* dv, void* ws, hipStream_t st) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t arr = up((size_t)d.H * d.ntot_pad * kHeadDim * sizeof(uint16_t));
   char* p = (char*)ws;
@@ -717,7 +736,7 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
   bwd_pack_kernel<<<pg, 256, 0, st>>>((const uint4*)v, (uint4*)vp, nullptr, d, nullptr, nullptr,
                                       0);
   bwd_rowstats_kernel<<<dim3(d.ntot_pad / 32, d.H), 256, 0, st>>>(
-      (const uint4*)o, (const uint4*)d_o, lse, lse2, lse2s, dd, d);
+      (const uint4*)o, (const float4*)o32, (const uint4*)d_o, lse, lse2, lse2s, dd, d);
   csr_t_count_kernel<<<dim3(d.B, d.H), 256, 0, st>>>(row_ptr, col_idx, d, counts);
   e = launch_scan_counts(counts, d.H * d.B, t_ptr, st);
   if (e != hipSuccess) return e;
@@ -725,7 +744,8 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
 
   BwdArgs a = {};
   a.qp = qp; a.qt = qt; a.dop = dop; a.dot = dot; a.kp = kp; a.kt = kt; a.vp = vp;
-  a.lse2 = lse2; a.lse2s = lse2s; a.dosig = dosig; a.dd = dd; a.dd_out = dd; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.lse2 = lse2; a.lse2s = lse2s; a.dosig = dosig; a.dd = dd; a.dd_out = dd;
+  a.d_given = o32 != nullptr; a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.t_ptr = t_ptr; a.t_list = t_list; a.dq = dq; a.dk = dk; a.dv = dv; a.d = d;
   if (d.b == 128) {
     a.n_items = d.H * (d.B + d.ns_pad / 128);

@@ -299,8 +299,30 @@ int bsga_attn_backward(const bsga_shape* shape, const uint16_t* q, const uint16_
   BSGA_TRY(check_ptr(dk, 16));
   BSGA_TRY(check_ptr(dv, 16));
   BSGA_TRY(check_ws(d, BSGA_OP_BACKWARD, ws, ws_bytes));
-  return hip_status(launch_backward(d, q, k, v, o, lse, d_o, row_ptr, col_idx, dq, dk, dv, ws,
-                                    (hipStream_t)stream));
+  return hip_status(launch_backward(d, q, k, v, o, nullptr, lse, d_o, row_ptr, col_idx, dq, dk,
+                                    dv, ws, (hipStream_t)stream));
+}
+
+int bsga_attn_backward_o32(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const float* o32, const float* lse,
+                           const uint16_t* d_o, const int32_t* row_ptr, const int32_t* col_idx,
+                           float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                           void* stream) {
+  BSGA_TRY(check_shape(shape));
+  const Dims d = make_dims(*shape);
+  BSGA_TRY(check_select_shape(d));
+  BSGA_TRY(check_qkv(q, k, v));
+  BSGA_TRY(check_ptr(o32, 16));
+  BSGA_TRY(check_ptr(d_o, 16));
+  BSGA_TRY(check_ptr(lse, 4));
+  BSGA_TRY(check_ptr(row_ptr, 4));
+  BSGA_TRY(check_ptr(col_idx, 4));
+  BSGA_TRY(check_ptr(dq, 16));
+  BSGA_TRY(check_ptr(dk, 16));
+  BSGA_TRY(check_ptr(dv, 16));
+  BSGA_TRY(check_ws(d, BSGA_OP_BACKWARD, ws, ws_bytes));
+  return hip_status(launch_backward(d, q, k, v, nullptr, o32, lse, d_o, row_ptr, col_idx, dq, dk,
+                                    dv, ws, (hipStream_t)stream));
 }
 
 int bsga_sparse_attn(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
@@ -450,10 +472,11 @@ int bsga_special_rows_packed(const bsga_shape* shape, const uint16_t* q, const v
                                         lse, ws, (hipStream_t)stream));
 }
 
-int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-               const double* rho_per_head, double rho, double tau, float* probs, int32_t* row_ptr,
-               int32_t* col_idx, int64_t col_capacity, uint16_t* o, float* lse, void* ws,
-               size_t ws_bytes, void* stream) {
+static int layer_impl(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const double* rho_per_head, double rho, double tau,
+                      float* probs, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                      uint16_t* o, float* lse, float* o32, bool train, void* ws,
+                      size_t ws_bytes, void* stream) {
   BSGA_TRY(check_shape(shape));
   const Dims d = make_dims(*shape);
   BSGA_TRY(check_select_shape(d));
@@ -462,6 +485,10 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, co
   BSGA_TRY(check_csr(d, row_ptr, col_idx, col_capacity));
   BSGA_TRY(check_ptr(o, 16));
   BSGA_TRY(check_ptr(lse, 4));
+  if (train) {
+    BSGA_TRY(check_ptr(o32, 16));
+    if (!patch_rows_train_supported(d)) return BSGA_ERR_UNSUPPORTED;
+  }
   SelectParams sp;
   BSGA_TRY(fill_select_params(d, rho_per_head, rho, tau, &sp));
   BSGA_TRY(check_ws(d, BSGA_OP_LAYER, ws, ws_bytes));
@@ -478,8 +505,25 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, co
   BSGA_TRY(hip_status(launch_select(d, probs, sp, row_ptr, col_idx, scratch, st)));
   BSGA_TRY(hip_status(launch_pack(d, k, v, kp, vt, st)));
   BSGA_TRY(hip_status(launch_patch_rows(d, q, kp, vt, row_ptr, col_idx, o, lse, st, scratch,
-                                        ws_bytes - ws_pack(d))));
-  return hip_status(launch_special_rows(d, q, kp, vt, o, lse, scratch, st));
+                                        ws_bytes - ws_pack(d), o32)));
+  return hip_status(launch_special_rows(d, q, kp, vt, o, lse, scratch, st, o32));
+}
+
+int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               const double* rho_per_head, double rho, double tau, float* probs, int32_t* row_ptr,
+               int32_t* col_idx, int64_t col_capacity, uint16_t* o, float* lse, void* ws,
+               size_t ws_bytes, void* stream) {
+  return layer_impl(shape, q, k, v, rho_per_head, rho, tau, probs, row_ptr, col_idx, col_capacity,
+                    o, lse, nullptr, false, ws, ws_bytes, stream);
+}
+
+int bsga_layer_train(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const double* rho_per_head, double rho, double tau,
+                     float* probs, int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                     uint16_t* o, float* lse, float* o32, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return layer_impl(shape, q, k, v, rho_per_head, rho, tau, probs, row_ptr, col_idx, col_capacity,
+                    o, lse, o32, true, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -167,10 +167,13 @@ hipError_t launch_nmse(const Dims& d, const uint16_t* ref, const uint16_t* out, 
                        void* ws, hipStream_t st);
 
 size_t backward_workspace(const Dims& d);
+// Exactly one of o (the bf16 rows; D = sum_k P dP is then recomputed by
+// dq_kernel) and o32 (float32 rows from the training-mode forward; D = dO . O
+// from them, and dq_kernel runs its gradient sweep only) is non-null.
 hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                           const uint16_t* o, const float* lse, const uint16_t* d_o,
-                           const int32_t* row_ptr, const int32_t* col_idx, float* dq, float* dk,
-                           float* dv, void* ws, hipStream_t st);
+                           const uint16_t* o, const float* o32, const float* lse,
+                           const uint16_t* d_o, const int32_t* row_ptr, const int32_t* col_idx,
+                           float* dq, float* dk, float* dv, void* ws, hipStream_t st);
 
 size_t pack_bytes(const Dims& d);  // packed K and V^T
 hipError_t launch_pack(const Dims& d, const uint16_t* k, const uint16_t* v,
@@ -182,14 +185,18 @@ hipError_t launch_sparse_attn(const Dims& d, const uint16_t* q,
 // ws (optional, patch_rows_workspace bytes): lets b = 128 rows of the last,
 // partial round of workgroups run as key-range pieces merged afterwards
 size_t patch_rows_workspace(const Dims& d);
+// o32 (training mode, needs ws; b = 128 or b = 64 with B <= 8192): P enters
+// P V as a float16 pair hi + lo and the final rows are also written as
+// float32 [H][N][64]
 hipError_t launch_patch_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                              const uint16_t* vt, const int32_t* row_ptr, const int32_t* col_idx,
                              uint16_t* o, float* lse, hipStream_t st, void* ws = nullptr,
-                             size_t ws_bytes = 0);
+                             size_t ws_bytes = 0, float* o32 = nullptr);
+bool patch_rows_train_supported(const Dims& d);
 size_t special_workspace(const Dims& d);
 hipError_t launch_special_rows(const Dims& d, const uint16_t* q, const uint16_t* kp,
                                const uint16_t* vt, uint16_t* o, float* lse, void* ws,
-                               hipStream_t st);
+                               hipStream_t st, float* o32 = nullptr);
 hipError_t launch_special(const Dims& d, const uint16_t* q,
                           const uint16_t* kp, const uint16_t* vt, uint16_t* o,
                           float* lse, void* ws, hipStream_t st);

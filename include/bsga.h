@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BSGA_VERSION 2
+#define BSGA_VERSION 3
 #define BSGA_MAX_HEADS 256     /* per-head budget table size */
 #define BSGA_MAX_BLOCKS 4096   /* largest B accepted by bsga_select */
 
@@ -377,6 +377,40 @@ int bsga_layer(const bsga_shape* shape, const uint16_t* q, const uint16_t* k,
                double tau, float* probs, int32_t* row_ptr, int32_t* col_idx,
                int64_t col_capacity, uint16_t* o, float* lse,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Training mode of bsga_layer ([BSGA] outlook: sparse attention inside
+ * training): the same mask and softmax, except that P enters the P V
+ * products as a float16 pair hi + lo (hi = fp16(w), lo = fp16(w - hi):
+ * about 22 significant bits of every weight, against 11 for hi alone), and
+ * every final row is also written as float32 to o32 ([H][N][64], 16-byte
+ * aligned, fully written); o holds bf16(o32), element for element.  o32 is
+ * what bsga_attn_backward_o32 takes to form D = dO . O without recomputing
+ * the softmax.  The P V products cost twice the matrix-core work and the
+ * split about half again the softmax's vector work.  Same arguments and
+ * workspace (BSGA_OP_LAYER) as bsga_layer; BSGA_ERR_UNSUPPORTED at b = 64
+ * with B > 8192 (the unpaired 64-row kernel has no training mode). */
+int bsga_layer_train(const bsga_shape* shape, const uint16_t* q,
+                     const uint16_t* k, const uint16_t* v,
+                     const double* rho_per_head, double rho, double tau,
+                     float* probs, int32_t* row_ptr, int32_t* col_idx,
+                     int64_t col_capacity, uint16_t* o, float* lse,
+                     float* o32, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* bsga_attn_backward with D = dO . O taken from the float32 rows o32 of
+ * bsga_layer_train (accurate to about 2^-22 of each weight) instead of
+ * recomputed as sum_k P dP by a first sweep of the dQ kernel over every
+ * kept key: the dQ kernel then runs its gradient sweep only.  Same
+ * arguments, layouts, precision (otherwise) and workspace as
+ * bsga_attn_backward, with o32 ([H][N][64] float32, 16-byte aligned) in
+ * place of o. */
+int bsga_attn_backward_o32(const bsga_shape* shape, const uint16_t* q,
+                           const uint16_t* k, const uint16_t* v,
+                           const float* o32, const float* lse,
+                           const uint16_t* d_o, const int32_t* row_ptr,
+                           const int32_t* col_idx, float* dq, float* dk,
+                           float* dv, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert bsga.version() == 2
+    assert bsga.version() == 3
     for s in range(6):
         assert bsga.status_string(s)
     assert bsga.status_string(99) == "unknown status"
@@ -262,6 +262,20 @@ def test_validation_before_launch():
     assert lib.bsga_special_dense(sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == bsga.ERR_WORKSPACE
     assert lib.bsga_layer(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE, FAKE,
                           FAKE, ws - 1, None) == bsga.ERR_WORKSPACE
+    # training mode: the float32 rows are required and 16-byte aligned
+    assert lib.bsga_layer_train(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE,
+                                FAKE, None, FAKE, ws, None) == bsga.ERR_INVALID_ARG
+    assert lib.bsga_layer_train(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE,
+                                FAKE, FAKE + 4, FAKE, ws, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_layer_train(sh, FAKE, FAKE, FAKE, None, 0.5, 0.9, FAKE, FAKE, FAKE, cap, FAKE,
+                                FAKE, FAKE, FAKE, ws - 1, None) == bsga.ERR_WORKSPACE
+    wsb = bsga.workspace_bytes(shape, bsga.OP_BACKWARD)
+    assert lib.bsga_attn_backward_o32(sh, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, wsb, None) == bsga.ERR_INVALID_ARG
+    assert lib.bsga_attn_backward_o32(sh, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, wsb, None) == bsga.ERR_MISALIGNED
+    assert lib.bsga_attn_backward_o32(sh, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, wsb - 1, None) == bsga.ERR_WORKSPACE
     # the selection without a workspace: its row limit, then the usual checks
     # (all before any HIP call)
     over = S(1, 128 * 1025, 0, 64, 128)  # 64 heads x 1025 blocks > 65,536 rows
