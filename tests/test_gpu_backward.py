@@ -105,8 +105,9 @@ def test_backward_dense_mask_equals_dense(lib):
             assert np.abs(g[h].cpu().numpy() - r).max() <= G_TOL * np.sqrt(np.mean(r ** 2))
 
 
+@pytest.mark.parametrize("via", ["sweep", "o32"])
 @pytest.mark.parametrize("index", [4, 5])
-def test_backward_full_size(lib, index):
+def test_backward_full_size(lib, index, via):
     """Full-size layers (100 frames, 78,200 tokens; 200 frames, 274,800
     tokens, per-head rho).  The oracle cannot afford every query row there,
     so:
@@ -122,7 +123,10 @@ def test_backward_full_size(lib, index):
       of magnitudes, plus for dK the effect of O's bf16 rounding on D_q
       (|dD_q| <= 2^-8 |dO_q| |O_q|), and for dV the float16 rounding of each
       weight P_qk (relative at most 2^-11, dO exact in float16), i.e.
-      (2^-11 + 1e-4) sum_q P_qk |dO_q|;
+      (2^-11 + 1e-4) sum_q P_qk |dO_q|.  With via = "o32" the forward is
+      bsga_layer_train and the backward bsga_attn_backward_o32: D_q = dO_q .
+      O_q from the float32 rows on both sides (the GPU sums its 64 products in
+      float32: |dD_q| <= 2^-16 |dO_q| |O_q| set aside instead of 2^-8);
     * over all keys of each head: sum_k dV_k = sum_q dO_q (softmax rows sum
       to one) within (2^-11 + 1e-5) sum_q |dO_q| (the float16 weights of a
       row sum to one within 2^-11 of their sum), and sum_k dK_k = 0 (a
@@ -137,19 +141,24 @@ def test_backward_full_size(lib, index):
     x = synth.generate(cfg)
     shape = layer_shape(cfg)
     q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
-    bufs = lib.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+    if via == "o32":
+        bufs, o_fwd = lib.layer_train(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+    else:
+        bufs = lib.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
+        o_fwd = bufs.o
     rng = np.random.default_rng(8000 + index)
     do_bits = synth.fp32_to_bf16_bits(rng.standard_normal((H, N, 64), dtype=np.float32))
     d_o = to_dev(do_bits)
-    dq, dk, dv = lib.attn_backward(shape, q, k, v, bufs.o, bufs.lse, d_o, bufs.row_ptr,
+    dq, dk, dv = lib.attn_backward(shape, q, k, v, o_fwd, bufs.lse, d_o, bufs.row_ptr,
                                    bufs.col_idx)
     torch.cuda.synchronize()
-    say("   layer and backward done")
+    say(f"   layer and backward done ({via})")
     B = lib.num_blocks(shape)
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     ci = bufs.col_idx.cpu().numpy()[:rp[-1]].astype(np.int64)
     lse_all = bufs.lse.cpu().numpy().astype(np.float64)
-    o_all = bufs.o
+    o_all = o_fwd
+    d_round = 2.0 ** -16 if via == "o32" else 2.0 ** -8  # the forward rows' rounding
     del q, k, v
     spec, patch = O.token_roles(cfg.frames, cfg.patches_per_frame, cfg.special_per_frame)
     n_p = patch.shape[0]
@@ -184,7 +193,7 @@ def test_backward_full_size(lib, index):
         rms = float(np.sqrt(np.mean(ref[rows] ** 2)))
         worst["dq"] = max(worst["dq"], float(np.abs(got - ref[rows]).max()) / rms)
         # --- dV, dK of sampled keys against the forward's LSE and O
-        oh = from_dev_bf16(o_all[h])
+        oh = o_all[h].double().cpu().numpy() if via == "o32" else from_dev_bf16(o_all[h])
         lse = lse_all[h]
         dd = np.sum(doh * oh, axis=1)
         seen_by = [[] for _ in range(B)]  # query blocks keeping each key block
@@ -211,7 +220,7 @@ def test_backward_full_size(lib, index):
             dk_ref = (p * (dp - dd[qs])) @ qh[qs] / 8.0
             b_dv = (2.0 ** -11 + 1e-4) * (p @ np.abs(doh[qs])) + 1e-30
             b_dk = (1e-4 * ((p * (np.abs(dp) + np.abs(dd[qs]))) @ np.abs(qh[qs]))
-                    + 2.0 ** -8 * (p * np.linalg.norm(doh[qs], axis=1)
+                    + d_round * (p * np.linalg.norm(doh[qs], axis=1)
                                    * np.linalg.norm(oh[qs], axis=1)) @ np.abs(qh[qs])) / 8.0
             worst["dv"] = max(worst["dv"], float((np.abs(dvg[r] - dv_ref) / b_dv).max()))
             worst["dk"] = max(worst["dk"], float((np.abs(dkg[r] - dk_ref) / b_dk).max()))
