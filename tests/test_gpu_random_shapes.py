@@ -26,7 +26,12 @@ Per shape, through the C ABI:
   with itself as the only match) has dQ and dK near 1e-30, and float32
   rounding of dS = P (dP - D), far below the terms' size, would count as
   error; the floor is still 2^-15 of that size, above the rounding of dS
-  (a bf16 pair hi + lo) in the dQ and dK products.
+  (a bf16 pair hi + lo) in the dQ and dK products;
+* training mode on the same shape: bsga_layer_train's mask equals
+  bsga_layer's, o = bf16(o32) element for element, every float32 row lies
+  within 2e-3 rms(O_dense) of the oracle (no rounding allowance; empty rows
+  0), and bsga_attn_backward_o32 from those rows meets the gradient bar
+  above.
 """
 from __future__ import annotations
 
@@ -41,6 +46,13 @@ pytestmark = pytest.mark.gpu
 O_TOL = 2e-2
 LSE_TOL = 2e-3
 G_TOL = 2e-2
+O32_TOL = 2e-3
+
+
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 def _shapes(n=16, seed=2024):
@@ -102,10 +114,20 @@ def test_random_shape(lib, shape):
     rng = np.random.default_rng(900 + i)
     do_bits = synth.fp32_to_bf16_bits(
         rng.standard_normal((heads, cfg.tokens, 64), dtype=np.float32))
-    grads = lib.attn_backward(shp, q, k, v, bufs.o, bufs.lse, to_dev(do_bits), bufs.row_ptr,
-                              bufs.col_idx)
+    d_o = to_dev(do_bits)
+    grads = lib.attn_backward(shp, q, k, v, bufs.o, bufs.lse, d_o, bufs.row_ptr, bufs.col_idx)
     probs2, scores = lib.predict_mask(shp, q, k, want_scores=True)
+    bufs_t, o32 = lib.layer_train(shp, q, k, v, rho, tau)
+    grads32 = lib.attn_backward(shp, q, k, v, o32, bufs_t.lse, d_o, bufs_t.row_ptr,
+                                bufs_t.col_idx)
     torch.cuda.synchronize()
+    assert torch.equal(bufs.probs, bufs_t.probs) and torch.equal(bufs.row_ptr, bufs_t.row_ptr)
+    nnz = int(bufs.row_ptr[-1])
+    assert torch.equal(bufs.col_idx[:nnz], bufs_t.col_idx[:nnz])
+    o32n = o32.cpu().numpy()
+    assert np.array_equal(_bf16_rne_bits(o32n),
+                          bufs_t.o.view(torch.int16).cpu().numpy().view(np.uint16)), "o != bf16(o32)"
+    g32 = [g.cpu().numpy() for g in grads32]
     assert torch.equal(bufs.probs, probs2)
     scores = scores.cpu().numpy()
     B = lib.num_blocks(shp)
@@ -119,6 +141,8 @@ def test_random_shape(lib, shape):
     _, patch = O.token_roles(frames, gh * gw, specials)
     worst_s = worst_p = worst_o = worst_l = worst_raw = 0.0
     worst_g = [0.0, 0.0, 0.0]
+    worst_g32 = [0.0, 0.0, 0.0]
+    worst_o32 = 0.0
     acc = cnt = 0.0
     def row_norm(a):
         return float(np.sqrt(np.mean(np.sum(a ** 2, axis=1))))
@@ -139,11 +163,16 @@ def test_random_shape(lib, shape):
         cnt += dense.size
         eo, el, _, _, raw = compare_rows(out, o[h], lse[h])
         worst_o, worst_l, worst_raw = max(worst_o, eo), max(worst_l, el), max(worst_raw, raw)
+        toks = np.fromiter(out.keys(), dtype=np.int64)
+        ro = np.stack([out[int(t)][0] for t in toks])
+        worst_o32 = max(worst_o32, float(np.abs(o32n[h][toks] - ro).max()))
         ref = O.attention_backward_head(qh, kh, vh, doh, frames, gh * gw, specials, block, kept)
         for j in range(3):
             rms = float(np.sqrt(np.mean(ref[j] ** 2)))
             err = float(np.abs(g_gpu[j][h] - ref[j]).max())
             worst_g[j] = max(worst_g[j], err / max(rms, 1e-3 * elem_scale[j], 1e-300))
+            err32 = float(np.abs(g32[j][h] - ref[j]).max())
+            worst_g32[j] = max(worst_g32[j], err32 / max(rms, 1e-3 * elem_scale[j], 1e-300))
             if rms < 1e-3 * elem_scale[j]:
                 say(f"   head {h} grad {'QKV'[j]}: rms {rms:.1e} below 1e-3 of its term scale "
                     f"{elem_scale[j]:.1e}; max err {err:.1e}")
@@ -152,6 +181,10 @@ def test_random_shape(lib, shape):
         f"O err beyond bf16 rounding "
         f"{worst_o / rms_o:.2e} rms (plain {worst_raw / rms_o:.2e}); "
         f"|dLSE| {worst_l:.1e}; grads dQ {worst_g[0]:.1e} dK {worst_g[1]:.1e} dV {worst_g[2]:.1e}")
+    say(f"   training mode: o32 err {worst_o32 / rms_o:.2e} rms; grads from o32 dQ "
+        f"{worst_g32[0]:.1e} dK {worst_g32[1]:.1e} dV {worst_g32[2]:.1e}")
     assert worst_s <= 1.0 and worst_p <= 1.0
     assert worst_o <= O_TOL * rms_o and worst_l <= LSE_TOL
     assert max(worst_g) <= G_TOL
+    assert worst_o32 <= O32_TOL * rms_o
+    assert max(worst_g32) <= G_TOL
