@@ -28,10 +28,11 @@
  * [i*b, min((i+1)*b, N_p)); B = ceil(N_p / b); the last block may be partial.
  *
  * Ownership: the caller owns and allocates every buffer, including the
- * workspace (size from bsga_workspace_bytes).  The library never allocates,
- * keeps no global state and never synchronises the host; every call only
- * enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
- * returns.  Inputs are read-only.
+ * workspace (size from bsga_workspace_bytes).  The library never allocates
+ * and never synchronises the host; every call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the null stream) and returns.  Inputs are
+ * read-only.  No state outlives a call, except the fixed device array of
+ * bsga_select_static (described there).
  *
  * Errors: every call returns a bsga_status.  All arguments are validated on
  * the host before anything is enqueued, so an error means nothing was
