@@ -74,5 +74,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_layer.c")
+C_CALLER = os.path.join(BUILD, "c_layer")
+
+
+def build_c_caller(out: str = C_CALLER, verbose: bool = False) -> str:
+    """Compile tests/c_layer.c, a plain C99 caller of bsga_layer that its GPU
+    test runs, against the in-tree libbsga.so (found through a run path
+    relative to the executable) and the HIP runtime."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    out_dir = os.path.dirname(os.path.abspath(out))
+    os.makedirs(out_dir, exist_ok=True)
+    rel = os.path.relpath(PKG, out_dir)
+    cmd = ["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+           "-D__HIP_PLATFORM_AMD__", "-isystem", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), C_CALLER_SRC,
+           "-L", PKG, "-lbsga", f"-Wl,-rpath,$ORIGIN/{rel}",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_CALLER_SRC}:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_caller(verbose=True)
