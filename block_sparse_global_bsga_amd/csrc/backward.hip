@@ -273,6 +273,29 @@ __device__ inline void load_cols(__amdgpu_buffer_rsrc_t rs, const TileOffsets& t
   }
 }
 
+// 32-token transposed tiles (64 dim rows of 4 chunks): chunk c of dim row r
+// sits at c ^ swz_c32(r), which depends on bits 1-3 of r only, so that the
+// operand reads of 8 and of 16 consecutive dim rows touch distinct banks.  A
+// 64-lane load covers 16 dim rows, lane -> (row lane / 4, chunk lane % 4).
+__device__ inline int swz_c32(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+__device__ inline uint32_t col32_tile_offset(int lane, uint32_t col_row_bytes) {
+  const int r = lane >> 2;
+  return (uint32_t)r * col_row_bytes + 16 * ((lane & 3) ^ swz_c32(r));
+}
+template <int NW>
+__device__ inline void load_cols32(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t row_bytes,
+                                   int col0, u32x4* lds, int w) {
+  constexpr int LPW = 4 / NW;  // 64 dims x 4 chunks = 4 blocks of 64 chunks
+  static_assert(LPW >= 1, "column tile loads");
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = LPW * w + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)((lds_u32x4*)lds + blk * 64), 16, off,
+                                             16 * blk * row_bytes + col0 * 2, 0, 0);
+  }
+}
+constexpr uint32_t kHalfCols32 = 32 * 4 * 16;  // 32 dims of a transposed 32-token tile, bytes
+
 // Per-lane LDS byte offsets of the MFMA A operands within a tile: row tiles
 // (K, V, Q, dO rows) at sub-tile 0 and k-step m, sub-tile t adding t * 32
 // rows; transposed 64-token tiles at the tokens of (sub-tile t, half h2) for
@@ -516,15 +539,19 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
 
 // ---------------------------------------------------------------------------
 // dK, dV: KT keys per workgroup (one patch block, or a tile of special keys),
-// 64-query tiles: for a patch key block the query blocks that keep it (from
-// the transposed CSR, QPB tiles each) then every special query tile; for
-// special keys every query tile.
-template <int KT>
-__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64, KT / 64))) void dkdv_kernel(
+// QT-query tiles: for a patch key block the query blocks that keep it (from
+// the transposed CSR, qpb tiles each) then every special query tile; for
+// special keys every query tile.  128-key workgroups take 64-query tiles;
+// 64-key workgroups (two waves) take 32-query tiles, whose two 16 KB LDS
+// slots let four workgroups, two waves per SIMD, share a compute unit
+// (64-query tiles would leave one).
+template <int KT, int QT>
+__global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     BwdArgs a, int qpb) {
-  constexpr int QT = 64, NW = KT / 32, NS = QT / 32, QCH = 8 * QT;
+  constexpr int NW = KT / 32, NS = QT / 32, QCH = 8 * QT;
   constexpr uint32_t kTile = QCH * 16;
-  static_assert(NW >= 2, "one 64-lane load per statistics row");
+  static_assert(QT == 64 || QT == 32, "query tile");
+  static_assert(QT == 32 || NW >= 2, "one 64-lane load per statistics row");
   // slot s: Q rows, dO rows, Q^T, dO^T, then lse2 and D
   __shared__ u32x4 smem[2 * 4 * QCH];
   __shared__ float stats[2][2][QT];
@@ -581,18 +608,42 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
   const __amdgpu_buffer_rsrc_t qtrs = buf_rsrc((const char*)a.qt + (size_t)h * 64 * trow, 64 * trow);
   const __amdgpu_buffer_rsrc_t otrs = buf_rsrc((const char*)a.dot + (size_t)h * 64 * trow, 64 * trow);
   const TileOffsets to = tile_offsets(lane, trow);
+  const uint32_t to_c32 = col32_tile_offset(lane, trow);
   const OperandOffsets op = operand_offsets(l32, hh);
+  // Q^T, dO^T operand chunks of dims l32 for sub-tile t, half h2 (add
+  // kHC for dims 32 + l32)
+  uint32_t colo[NS][2];
+  constexpr uint32_t kHC = QT == 64 ? kHalfCols : kHalfCols32;
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      colo[t][h2] = QT == 64 ? op.col[t][h2]
+                             : (uint32_t)(4 * l32 + ((2 * h2 + hh) ^ swz_c32(l32))) * 16;
   auto issue = [&](int qp0, int slot) {
     u32x4* base = smem + slot * 4 * QCH;
     load_rows<QT, NW>(qrs, to, qp0, base, w);
     load_rows<QT, NW>(ors, to, qp0, base + QCH, w);
-    load_cols<NW>(qtrs, to, trow, qp0, base + 2 * QCH, w);
-    load_cols<NW>(otrs, to, trow, qp0, base + 3 * QCH, w);
-    // lse2 and D of the tile's 64 queries: one 4-byte direct-to-LDS load per
-    // lane, issued by waves 0 and 1 (no register round trip, no extra wait)
-    if (w < 2)
-      __builtin_amdgcn_global_load_lds((const void*)((w == 0 ? a.lse2s : a.dd) + hrow + qp0 + lane),
-                                       (lds_void*)&stats[slot][w][0], 4, 0, 0);
+    if constexpr (QT == 64) {
+      load_cols<NW>(qtrs, to, trow, qp0, base + 2 * QCH, w);
+      load_cols<NW>(otrs, to, trow, qp0, base + 3 * QCH, w);
+      // lse2 and D of the tile's 64 queries: one 4-byte direct-to-LDS load
+      // per lane, issued by waves 0 and 1 (no register round trip, no extra
+      // wait)
+      if (w < 2)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)((w == 0 ? a.lse2s : a.dd) + hrow + qp0 + lane),
+            (lds_void*)&stats[slot][w][0], 4, 0, 0);
+    } else {
+      load_cols32<NW>(qtrs, to_c32, trow, qp0, base + 2 * QCH, w);
+      load_cols32<NW>(otrs, to_c32, trow, qp0, base + 3 * QCH, w);
+      // lse2 (lanes 0-31) and D (lanes 32-63) of the tile's 32 queries from
+      // wave 0: the two 32-float rows of stats[slot] are contiguous
+      if (w == 0)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)((hh ? a.dd : a.lse2s) + hrow + qp0 + l32),
+            (lds_void*)&stats[slot][0][0], 4, 0, 0);
+    }
   };
 
   // Query tiles alternate between two LDS slots; iterations come in pairs so
@@ -645,10 +696,10 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(KT / 64,
 #pragma unroll
           for (int e = 0; e < 8; ++e) rem[e] = s8[e] - (float)sb[e];
           const bf16x8 sl = __builtin_convertvector(rem, bf16x8);
-          const f16x8 o0 = lds_op16(smem, otb + op.col[t][h2]);
-          const f16x8 o1 = lds_op16(smem, otb + op.col[t][h2] + kHalfCols);
-          const bf16x8 q0 = lds_op(smem, qtb + op.col[t][h2]);
-          const bf16x8 q1 = lds_op(smem, qtb + op.col[t][h2] + kHalfCols);
+          const f16x8 o0 = lds_op16(smem, otb + colo[t][h2]);
+          const f16x8 o1 = lds_op16(smem, otb + colo[t][h2] + kHC);
+          const bf16x8 q0 = lds_op(smem, qtb + colo[t][h2]);
+          const bf16x8 q1 = lds_op(smem, qtb + colo[t][h2] + kHC);
           v0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(o0, pf, v0, 0, 0, 0);
           v1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(o1, pf, v1, 0, 0, 0);
           k0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0, sb, k0, 0, 0, 0);
@@ -755,12 +806,12 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
     a.n_items = d.H * (d.B + d.ns_pad / 128);
     dq_kernel<128><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 128);
-    dkdv_kernel<128><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
+    dkdv_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
   } else {
     a.n_items = d.H * (d.B + d.ns_pad / 64);
     dq_kernel<64><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 64);
-    dkdv_kernel<64><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 1);
+    dkdv_kernel<64, 32><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 2);
   }
   return hipGetLastError();
 }
