@@ -356,14 +356,18 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------------------
 // dQ: QT queries per workgroup (one patch block, or a tile of special
-// queries), 64-key tiles: the kept blocks (TPB tiles each) then the special
+// queries), KT-key tiles: the kept blocks (TPB tiles each) then the special
 // tiles for patch queries, every tile for special queries.
-// 128-row workgroups run three waves per SIMD (48 KB of LDS each, 168 VGPRs).
-template <int QT>
+// 128-row workgroups take 64-key tiles and run three waves per SIMD (48 KB
+// of LDS each, 168 VGPRs); 64-row workgroups (two waves) take 32-key tiles,
+// whose 24 KB of LDS let four of them, two waves per SIMD, share a compute
+// unit (64-key tiles would leave three).
+template <int QT, int KT>
 __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 128 ? 3 : 2,
                                                                          QT == 128 ? 3 : 2))) void dq_kernel(
     BwdArgs a) {
-  constexpr int KT = 64, NW = QT / 32, NS = KT / 32, KCH = 8 * KT, TPB = QT / KT;
+  constexpr int NW = QT / 32, NS = KT / 32, KCH = 8 * KT, TPB = QT / KT;
+  static_assert(KT == 64 || KT == 32, "key tile");
   constexpr uint32_t kTile = KCH * 16;   // bytes of one tile
   __shared__ u32x4 smem[2 * 3 * KCH];  // slot s: K rows, V rows, K^T
   const Dims& d = a.d;
@@ -422,11 +426,25 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
   const __amdgpu_buffer_rsrc_t ktrs = buf_rsrc((const char*)a.kt + (size_t)h * 64 * trow, 64 * trow);
   const TileOffsets to = tile_offsets(lane, trow);
   const OperandOffsets op = operand_offsets(l32, hh);
+  // K^T operand chunks of dims l32 for sub-tile t, half h2 (add kHC for
+  // dims 32 + l32)
+  uint32_t colo[NS][2];
+  constexpr uint32_t kHC = KT == 64 ? kHalfCols : kHalfCols32;
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      colo[t][h2] = KT == 64 ? op.col[t][h2]
+                             : (uint32_t)(4 * l32 + ((2 * h2 + hh) ^ swz_c32(l32))) * 16;
+  const uint32_t to_c32 = col32_tile_offset(lane, trow);
   auto issue = [&](int kp0, int slot, bool with_kt) {
     u32x4* base = smem + slot * 3 * KCH;
     load_rows<KT, NW>(krs, to, kp0, base, w);
     load_rows<KT, NW>(vrs, to, kp0, base + KCH, w);
-    if (with_kt) load_cols<NW>(ktrs, to, trow, kp0, base + 2 * KCH, w);
+    if (with_kt) {
+      if constexpr (KT == 64) load_cols<NW>(ktrs, to, trow, kp0, base + 2 * KCH, w);
+      else load_cols32<NW>(ktrs, to_c32, trow, kp0, base + 2 * KCH, w);
+    }
   };
 
   // Two sweeps over the key tiles.  The first accumulates D = sum_k P dP,
@@ -489,8 +507,8 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
 #pragma unroll
             for (int e = 0; e < 8; ++e) rem[e] = e8[e] - (float)ds_hi[e];
             const bf16x8 ds_lo = __builtin_convertvector(rem, bf16x8);
-            const bf16x8 k0 = lds_op(smem, ktb + op.col[t][h2]);
-            const bf16x8 k1 = lds_op(smem, ktb + op.col[t][h2] + kHalfCols);
+            const bf16x8 k0 = lds_op(smem, ktb + colo[t][h2]);
+            const bf16x8 k1 = lds_op(smem, ktb + colo[t][h2] + kHC);
             g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_hi, g0, 0, 0, 0);
             g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, ds_hi, g1, 0, 0, 0);
             g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ds_lo, g0, 0, 0, 0);
@@ -804,12 +822,12 @@ hipError_t launch_backward(const Dims& d, const uint16_t* q, const uint16_t* k, 
   a.t_ptr = t_ptr; a.t_list = t_list; a.dq = dq; a.dk = dk; a.dv = dv; a.d = d;
   if (d.b == 128) {
     a.n_items = d.H * (d.B + d.ns_pad / 128);
-    dq_kernel<128><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
+    dq_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 128);
     dkdv_kernel<128, 64><<<xcd_grid(a.n_items), 256, 0, st>>>(a, 2);
   } else {
     a.n_items = d.H * (d.B + d.ns_pad / 64);
-    dq_kernel<64><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
+    dq_kernel<64, 32><<<xcd_grid(a.n_items), 128, 0, st>>>(a);
     a.n_items = d.H * (d.B + d.ns_pad / 64);
     dkdv_kernel<64, 32><<<xcd_grid(a.n_items), 128, 0, st>>>(a, 2);
   }
