@@ -436,7 +436,7 @@ __global__ __launch_bounds__(2 * QT) __attribute__((amdgpu_waves_per_eu(QT == 12
     for (int h2 = 0; h2 < 2; ++h2)
       colo[t][h2] = KT == 64 ? op.col[t][h2]
                              : (uint32_t)(4 * l32 + ((2 * h2 + hh) ^ swz_c32(l32))) * 16;
-  const uint32_t to_c32 = col32_tile_offset(lane, trow);
+  const uint32_t to_c32 = KT == 32 ? col32_tile_offset(lane, trow) : 0u;
   auto issue = [&](int kp0, int slot, bool with_kt) {
     u32x4* base = smem + slot * 3 * KCH;
     load_rows<KT, NW>(krs, to, kp0, base, w);
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(2 * KT) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const __amdgpu_buffer_rsrc_t qtrs = buf_rsrc((const char*)a.qt + (size_t)h * 64 * trow, 64 * trow);
   const __amdgpu_buffer_rsrc_t otrs = buf_rsrc((const char*)a.dot + (size_t)h * 64 * trow, 64 * trow);
   const TileOffsets to = tile_offsets(lane, trow);
-  const uint32_t to_c32 = col32_tile_offset(lane, trow);
+  const uint32_t to_c32 = QT == 32 ? col32_tile_offset(lane, trow) : 0u;
   const OperandOffsets op = operand_offsets(l32, hh);
   // Q^T, dO^T operand chunks of dims l32 for sub-tile t, half h2 (add
   // kHC for dims 32 + l32)
