@@ -15,7 +15,10 @@ Checks, through bsga_layer (the kernel sequence bench.py times):
 * outputs: the first, the last and one seeded query block against the
   oracle, to the bar of the other parity tests (2e-2 rms(O_dense) once half
   an ulp of each stored bf16 value is set aside; |dLSE| <= 2e-3), rms(O_dense)
-  over the same rows from the dense softmax over all 524,293 (262,149) keys.
+  over the same rows from the dense softmax over all 524,293 (262,149) keys;
+* training mode at the same size (bsga_layer_train): the mask equals
+  bsga_layer's, o = bf16(o32) element for element, and the float32 rows of
+  the same query blocks lie within 2e-3 rms(O_dense) of the oracle.
 """
 from __future__ import annotations
 
@@ -29,6 +32,13 @@ pytestmark = pytest.mark.gpu
 
 O_TOL = 2e-2
 LSE_TOL = 2e-3
+O32_TOL = 2e-3
+
+
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 @pytest.mark.parametrize("block, grid_w", [(128, 1024), (64, 512)])
@@ -56,7 +66,15 @@ def test_max_blocks(block, grid_w):
         assert np.array_equal(ci[rp[i]:rp[i + 1]], ref), i
     say(f"   masks: all {B} rows bit-exact, {kh} blocks per row")
     o, lse = from_dev_bf16(bufs.o[0]), bufs.lse[0].cpu().numpy()
-    del bufs, q, k, v
+    # training mode on the same inputs
+    tb, o32 = bsga.layer_train(shape, q, k, v, cfg.rho, cfg.tau)
+    torch.cuda.synchronize()
+    assert torch.equal(tb.row_ptr, bufs.row_ptr)
+    assert torch.equal(tb.col_idx[:int(rp[-1])], bufs.col_idx[:int(rp[-1])])
+    o32n = o32[0].cpu().numpy()
+    assert np.array_equal(_bf16_rne_bits(o32n),
+                          tb.o[0].view(torch.int16).cpu().numpy().view(np.uint16)), "o != bf16(o32)"
+    del bufs, tb, o32, q, k, v
     torch.cuda.empty_cache()
     blocks = sorted({0, B - 1, int(np.random.default_rng(4600 + block).integers(1, B - 1))})
     qh, kh_, vh = head_f64(x, 0)
@@ -70,7 +88,11 @@ def test_max_blocks(block, grid_w):
         acc += float(np.sum(dense ** 2))
     rms = (acc / (toks.size * 64)) ** 0.5
     eo, el, _, _, raw = compare_rows(out, o, lse)
+    ro = np.stack([out[int(t)][0] for t in toks])
+    e32 = float(np.abs(o32n[toks] - ro).max())
     say(f"   query blocks {blocks}: err beyond bf16 rounding {eo / rms:.3e} rms(O_dense) "
-        f"(plain {raw / rms:.3e}), max|dLSE| = {el:.3e}")
+        f"(plain {raw / rms:.3e}), max|dLSE| = {el:.3e}; training mode: mask equal, "
+        f"o = bf16(o32), o32 err {e32 / rms:.3e} rms(O_dense)")
     assert eo <= O_TOL * rms
     assert el <= LSE_TOL
+    assert e32 <= O32_TOL * rms
