@@ -133,12 +133,30 @@ def test_backward_full_size(lib, index, via):
       query's dS sum to zero) within 1e-5 of sum_q |q_q| |dO_q| max_k |v_k| /
       8: a row's float32 weights sum to one within about 1e-6, and D is
       formed from the same weights as dS."""
+    _full_size_backward(lib, synth.generate(synth.CONFIGS[index]), via, 8000 + index)
+
+
+@pytest.mark.parametrize("via", ["sweep", "o32"])
+@pytest.mark.parametrize("block, grid_w", [(128, 1024), (64, 512)])
+def test_backward_max_blocks(lib, block, grid_w, via):
+    """The largest block count the selection takes, B = 4096 (the layers of
+    test_gpu_max_sizes: one frame of 512 x 1024 patches at b = 128, 512 x 512
+    at b = 64, five special tokens, rho 0.99, tau 0, 40 kept blocks per row):
+    the transposed mask at its largest, through both backward calls, to the
+    checks of test_backward_full_size (dQ rows of sampled query blocks exact
+    against the oracle, dV and dK of sampled keys against the gradient
+    formulas, the column sums over every key)."""
+    x = synth.random_layer(1, 512, grid_w, 1, block, seed=4500 + block, special_per_frame=5,
+                           kind="diffuse", rho=0.99, tau=0.0)
+    _full_size_backward(lib, x, via, 8100 + block)
+
+
+def _full_size_backward(lib, x, via, seed):
     import torch
     from gpu_helpers import from_dev_bf16, head_f64, layer_shape, say, to_dev
-    cfg = synth.CONFIGS[index]
+    cfg = x.cfg
     H, N = cfg.heads, cfg.tokens
-    say(f"[backward-full-size] {cfg.name}: N={N} H={H} b={cfg.block}")
-    x = synth.generate(cfg)
+    say(f"[backward-full-size] {cfg.name}: N={N} H={H} b={cfg.block} ({via})")
     shape = layer_shape(cfg)
     q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
     if via == "o32":
@@ -146,7 +164,7 @@ def test_backward_full_size(lib, index, via):
     else:
         bufs = lib.layer(shape, q, k, v, cfg.rho, cfg.tau, x.rho_per_head)
         o_fwd = bufs.o
-    rng = np.random.default_rng(8000 + index)
+    rng = np.random.default_rng(seed)
     do_bits = synth.fp32_to_bf16_bits(rng.standard_normal((H, N, 64), dtype=np.float32))
     d_o = to_dev(do_bits)
     dq, dk, dv = lib.attn_backward(shape, q, k, v, o_fwd, bufs.lse, d_o, bufs.row_ptr,
