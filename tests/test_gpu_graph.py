@@ -9,6 +9,8 @@ small size: the graph is replayed three times, with eager layer calls on other
 inputs and synchronisations between the replays, and every replay's mask
 (probabilities and CSR), O and LSE must equal the eager call on the same
 inputs byte for byte.  The replay time is printed beside the eager time.
+A training step (bsga_layer_train, then bsga_attn_backward_o32) is captured
+the same way, at b = 64 (aligned pairs) and b = 128.
 """
 from __future__ import annotations
 
@@ -85,3 +87,76 @@ def test_layer_graph_replay(name):
     torch.cuda.synchronize()
     say(f"[graph] {name}: 3 replays byte-equal to the eager layer; replay "
         f"{ev[0].elapsed_time(ev[1]) / 10:.4f} ms, eager {ev[1].elapsed_time(ev[2]) / 10:.4f} ms")
+
+
+@pytest.mark.parametrize("name", ["vggt-8f", "ragged-b128"])
+def test_training_step_graph_replay(name):
+    """A training step, bsga_layer_train then bsga_attn_backward_o32 on the
+    float32 rows, captured into one HIP graph with every buffer (outputs,
+    gradients, workspaces) allocated beforehand: three replays, with eager
+    steps on other inputs and synchronisations between them, must each
+    reproduce the eager step byte for byte (mask, O, LSE, float32 rows, dQ,
+    dK, dV)."""
+    import torch
+    from block_sparse_global_bsga_amd import bsga
+    from gpu_helpers import layer_shape, say, to_dev
+    if name == "vggt-8f":
+        x = synth.generate(synth.CONFIGS[2])
+    else:
+        x = synth.random_layer(3, 10, 13, 2, 128, seed=11, kind="corr", special_per_frame=5)
+    cfg = x.cfg
+    shape = layer_shape(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    rng = np.random.default_rng(cfg.seed + 7)
+    d_o = to_dev(synth.fp32_to_bf16_bits(rng.standard_normal(x.q.shape, dtype=np.float32)))
+    q2 = to_dev(synth.fp32_to_bf16_bits(rng.standard_normal(x.q.shape, dtype=np.float32)))
+
+    def new_outputs():
+        return (bsga.LayerBuffers(shape, dev), torch.empty(x.q.shape, dtype=torch.float32, device=dev),
+                [torch.empty(x.q.shape, dtype=torch.float32, device=dev) for _ in range(3)],
+                bsga.workspace(shape, bsga.OP_BACKWARD, dev))
+
+    def step(qq, outs):
+        bufs, o32, g, ws = outs
+        bsga.layer_train(shape, qq, k, v, cfg.rho, cfg.tau, bufs=bufs, o32=o32)
+        bsga.attn_backward(shape, qq, k, v, o32, bufs.lse, d_o, bufs.row_ptr, bufs.col_idx,
+                           dq=g[0], dk=g[1], dv=g[2], ws=ws)
+
+    def snap(outs):
+        bufs, o32, g, _ = outs
+        nnz = int(bufs.row_ptr[-1])
+        return [t.clone() for t in (bufs.probs, bufs.row_ptr, bufs.col_idx[:nnz],
+                                    bufs.o.view(torch.int16), bufs.lse, o32, *g)]
+
+    ref = new_outputs()
+    step(q, ref)
+    torch.cuda.synchronize()
+    want = snap(ref)
+    outs, other = new_outputs(), new_outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(q, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(q, outs)
+    torch.cuda.synchronize()
+    names = ("probs", "row_ptr", "col_idx", "o", "lse", "o32", "dq", "dk", "dv")
+    for rep in range(3):
+        bufs, o32, g, _ = outs
+        bufs.o.view(torch.int16).fill_(0x7fc0)
+        bufs.lse.fill_(-1.0)
+        o32.fill_(float("nan"))
+        for t in g:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for w, got, n in zip(want, snap(outs), names):
+            assert torch.equal(w, got), (name, rep, n)
+        step(q2, other)
+        torch.cuda.synchronize()
+    say(f"[graph] training step {cfg.name}: 3 replays byte-equal to the eager step")
