@@ -359,7 +359,7 @@ struct BwdArgs {
 // queries), KT-key tiles: the kept blocks (TPB tiles each) then the special
 // tiles for patch queries, every tile for special queries.
 // 128-row workgroups take 64-key tiles and run three waves per SIMD (48 KB
-// of LDS each, 168 VGPRs); 64-row workgroups (two waves) take 32-key tiles,
+// of LDS each, 159 VGPRs); 64-row workgroups (two waves) take 32-key tiles,
 // whose 24 KB of LDS let four of them, two waves per SIMD, share a compute
 // unit (64-key tiles would leave three).
 template <int QT, int KT>
